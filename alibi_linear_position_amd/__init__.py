@@ -1,0 +1,179 @@
+"""Python binding of libalibi, the gfx950 causal ALiBi attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/alibi.h. PyTorch provides device memory and
+the current stream. There is no fallback: if libalibi.so has not been built,
+or a call returns an error status, these functions raise.
+
+    slopes(H)                          -> float32 CPU tensor (host generator)
+    attn_fwd(q, k, v, slopes, causal)  -> bf16 (B, H, N, d)
+    attn_fwd_f32(q, k, v, slopes, causal)
+    attn_decode(q, kcache, vcache, slopes)  -> bf16 (B, H, d)
+    attn_weights_f32(q, k, slopes, causal)  -> fp32 (B, H, N, N), test only
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libalibi.so")
+
+ALIBI_OK = 0
+_STATUS = {0: "ALIBI_OK", -1: "ALIBI_EINVAL", -2: "ALIBI_ENOTSUP", -3: "ALIBI_EHIP", -4: "ALIBI_ENOMEM"}
+
+# (name, argtypes) of every entry point declared in include/alibi.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+EXPORTS = {
+    "alibi_slopes": [_I, _P],
+    "alibi_attn_fwd": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
+    "alibi_attn_fwd_f32": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
+    "alibi_attn_decode": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
+    "alibi_attn_weights_f32": [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
+    "alibi_status_string": [_I],
+    "alibi_release": [],
+}
+
+_lib = None
+
+
+class AlibiError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libalibi.so (once) and declare its signatures. Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m alibi_linear_position_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, argtypes in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_char_p if name == "alibi_status_string" else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn_name, status):
+    if status != ALIBI_OK:
+        msg = load_library().alibi_status_string(status).decode()
+        raise AlibiError(fn_name, status, msg)
+
+
+def status_string(status: int) -> str:
+    return load_library().alibi_status_string(int(status)).decode()
+
+
+def slopes(H: int):
+    """Per-head slopes from the library's host generator (float32 CPU tensor)."""
+    import torch
+    out = torch.empty(int(H), dtype=torch.float32)
+    _check("alibi_slopes", load_library().alibi_slopes(int(H), ctypes.c_void_p(out.data_ptr())))
+    return out
+
+
+def _stream_handle(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, ndim, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _slopes_dev(slopes_t, H, device):
+    import torch
+    if slopes_t is None:
+        slopes_t = slopes(H)
+    s = slopes_t.to(device=device, dtype=torch.float32).contiguous()
+    if s.numel() != H:
+        raise ValueError(f"expected {H} slopes, got {s.numel()}")
+    return s
+
+
+def _fwd(entry, dtype, q, k, v, slopes_t, causal, out):
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, dtype, 4, n)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have one shape (B, H, N, d)")
+    B, H, N, d = q.shape
+    s = _slopes_dev(slopes_t, H, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, dtype, 4, "out")
+    with torch.cuda.device(q.device):
+        st = getattr(load_library(), entry)(
+            _P(q.data_ptr()), _P(k.data_ptr()), _P(v.data_ptr()), _P(out.data_ptr()),
+            B, H, N, d, _P(s.data_ptr()), int(bool(causal)), _stream_handle(q.device))
+    _check(entry, st)
+    return out
+
+
+def attn_fwd(q, k, v, slopes=None, causal=True, out=None):
+    """Fused ALiBi attention forward, bf16 (B, H, N, d) device tensors."""
+    import torch
+    return _fwd("alibi_attn_fwd", torch.bfloat16, q, k, v, slopes, causal, out)
+
+
+def attn_fwd_f32(q, k, v, slopes=None, causal=True, out=None):
+    """fp32 ALiBi attention forward (generic kernel)."""
+    import torch
+    return _fwd("alibi_attn_fwd_f32", torch.float32, q, k, v, slopes, causal, out)
+
+
+def attn_decode(q, kcache, vcache, slopes=None, out=None):
+    """Single-query decode: q (B, H, d), caches (B, H, L, d), bf16 device tensors."""
+    import torch
+    _need(q, torch.bfloat16, 3, "q")
+    _need(kcache, torch.bfloat16, 4, "kcache")
+    _need(vcache, torch.bfloat16, 4, "vcache")
+    B, H, L, d = kcache.shape
+    if vcache.shape != kcache.shape or tuple(q.shape) != (B, H, d):
+        raise ValueError("expected q (B, H, d) and caches (B, H, L, d)")
+    s = _slopes_dev(slopes, H, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, torch.bfloat16, 3, "out")
+    with torch.cuda.device(q.device):
+        st = load_library().alibi_attn_decode(
+            _P(q.data_ptr()), _P(kcache.data_ptr()), _P(vcache.data_ptr()), _P(out.data_ptr()),
+            B, H, L, d, _P(s.data_ptr()), _stream_handle(q.device))
+    _check("alibi_attn_decode", st)
+    return out
+
+
+def attn_weights_f32(q, k, slopes=None, causal=True):
+    """Test-only: materialised fp32 weights (B, H, N, N) of the fp32 forward."""
+    import torch
+    _need(q, torch.float32, 4, "q")
+    _need(k, torch.float32, 4, "k")
+    B, H, N, d = q.shape
+    s = _slopes_dev(slopes, H, q.device)
+    w = torch.empty((B, H, N, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = load_library().alibi_attn_weights_f32(
+            _P(q.data_ptr()), _P(k.data_ptr()), _P(w.data_ptr()), B, H, N, d,
+            _P(s.data_ptr()), int(bool(causal)), _stream_handle(q.device))
+    _check("alibi_attn_weights_f32", st)
+    return w
+
+
+def release():
+    _check("alibi_release", load_library().alibi_release())

@@ -1,0 +1,65 @@
+"""Build libalibi.so in-tree with hipcc for gfx950.
+
+    python -m alibi_linear_position_amd.build          # or build() from Python
+
+Every HIP source under csrc/ is compiled with -O3 for gfx950 only, with the
+packed-fp32 instruction feature disabled, and linked into one shared library
+next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libalibi.so")
+ARCH = "gfx950"
+
+SOURCES = ["api.cpp", "fwd_generic.hip", "fwd_mfma.hip", "decode.hip"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libalibi)")
+
+
+def compile_flags():
+    return [
+        "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+        "-I", INCLUDE, "-I", CSRC,
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libalibi.so; returns its path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="alibi_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            cmd = [cc, *compile_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            objs.append(obj)
+        tmp_lib = LIB + ".tmp"
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

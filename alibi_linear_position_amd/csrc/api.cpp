@@ -1,0 +1,177 @@
+// C-ABI entry points of libalibi (declared in include/alibi.h): argument
+// validation, the host slope generator, kernel selection and the per-device
+// decode workspace. Validation touches no HIP API, so argument errors are
+// reported identically on machines without a GPU.
+#include "alibi.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxLen = 1 << 24;  // token distances stay exact in fp32
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("ALIBI_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+// Softmax scale in log2 units: log2(e) / sqrt(d), evaluated in double.
+float scale_log2(int d) { return float(1.4426950408889634 / std::sqrt(double(d))); }
+
+int check_common(const void* a, const void* b, const void* c, const void* out, const float* slopes,
+                 int B, int H, int N, int d, uintptr_t align) {
+  if (!a || !b || !c || !out || !slopes) return ALIBI_EINVAL;
+  if (B < 1 || H < 1 || N < 1 || d < 1 || N > kMaxLen) return ALIBI_EINVAL;
+  if (!aligned(a, align) || !aligned(b, align) || !aligned(c, align) || !aligned(out, align))
+    return ALIBI_EINVAL;
+  if (!aligned(slopes, 4)) return ALIBI_EINVAL;
+  // grid sizes: one wave per row (generic) or per (b, h, block) -- keep them in 32 bits
+  if ((long long)B * H * N > (1LL << 31) * 4) return ALIBI_ENOTSUP;
+  return ALIBI_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ALIBI_OK : ALIBI_EHIP; }
+
+// ---- decode workspace: one growable buffer per device ----
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+
+int workspace_get(size_t bytes, float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ALIBI_EHIP;
+  if ((size_t)dev >= g_ws.size()) g_ws.resize(dev + 1);
+  Workspace& w = g_ws[dev];
+  if (w.bytes < bytes) {
+    if (w.ptr) {
+      // an earlier asynchronous decode may still read the old buffer
+      if (hipDeviceSynchronize() != hipSuccess) return ALIBI_EHIP;
+      if (hipFree(w.ptr) != hipSuccess) return ALIBI_EHIP;
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
+      w.ptr = nullptr;
+      (void)hipGetLastError();
+      return ALIBI_ENOMEM;
+    }
+    w.bytes = bytes;
+  }
+  *out = static_cast<float*>(w.ptr);
+  return ALIBI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int alibi_slopes(int H, float* slopes_out) {
+  if (H < 1 || slopes_out == nullptr) return ALIBI_EINVAL;
+  auto pow2_schedule = [](int n, int h) { return std::exp2(-8.0 * double(h + 1) / double(n)); };
+  int c = 1;
+  while (c * 2 <= H) c *= 2;
+  for (int h = 0; h < c; ++h) slopes_out[h] = float(pow2_schedule(c, h));
+  for (int t = 0; t < H - c; ++t) slopes_out[c + t] = float(pow2_schedule(2 * c, 2 * t));
+  return ALIBI_OK;
+}
+
+int alibi_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
+                   int d, const float* slopes, int causal, hipStream_t stream) {
+  int st = check_common(q, k, v, out, slopes, B, H, N, d, 16);
+  if (st != ALIBI_OK) return st;
+  if (causal != 0 && causal != 1) return ALIBI_EINVAL;
+  if (d > 256 || d % 8 != 0) return ALIBI_ENOTSUP;
+  const float c1 = scale_log2(d);
+  if (d == 64 || d == 128) {
+    if (log_enabled()) std::fprintf(stderr, "[alibi] fwd mfma B=%d H=%d N=%d d=%d causal=%d\n", B, H, N, d, causal);
+    return hip_status(alibi::launch_fwd_mfma(q, k, v, out, B, H, N, d, slopes, causal, c1, stream));
+  }
+  if (log_enabled()) std::fprintf(stderr, "[alibi] fwd generic bf16 B=%d H=%d N=%d d=%d\n", B, H, N, d);
+  return hip_status(alibi::launch_fwd_generic_bf16(q, k, v, out, B, H, N, d, slopes, causal, c1, stream));
+}
+
+int alibi_attn_fwd_f32(const float* q, const float* k, const float* v, float* out, int B, int H,
+                       int N, int d, const float* slopes, int causal, hipStream_t stream) {
+  int st = check_common(q, k, v, out, slopes, B, H, N, d, 4);
+  if (st != ALIBI_OK) return st;
+  if (causal != 0 && causal != 1) return ALIBI_EINVAL;
+  if (d > 256) return ALIBI_ENOTSUP;
+  return hip_status(alibi::launch_fwd_generic_f32(q, k, v, out, B, H, N, d, slopes, causal,
+                                                  scale_log2(d), stream));
+}
+
+int alibi_attn_decode(const void* q, const void* kcache, const void* vcache, void* out, int B,
+                      int H, int L, int d, const float* slopes, hipStream_t stream) {
+  int st = check_common(q, kcache, vcache, out, slopes, B, H, L, d, 16);
+  if (st != ALIBI_OK) return st;
+  if (d > 256 || d % 8 != 0) return ALIBI_ENOTSUP;
+  int splits = 1, chunk = L;
+  alibi::decode_plan(B, H, L, d, &splits, &chunk);
+  float* ws = nullptr;
+  if (splits > 1) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    const size_t bytes = (size_t)B * H * splits * (d + 2) * sizeof(float);
+    st = workspace_get(bytes, &ws);
+    if (st != ALIBI_OK) return st;
+  }
+  if (log_enabled())
+    std::fprintf(stderr, "[alibi] decode B=%d H=%d L=%d d=%d splits=%d chunk=%d\n", B, H, L, d, splits, chunk);
+  return hip_status(alibi::launch_decode(q, kcache, vcache, out, ws, B, H, L, d, splits, chunk, slopes,
+                                         scale_log2(d), stream));
+}
+
+int alibi_attn_weights_f32(const float* q, const float* k, float* w, int B, int H, int N, int d,
+                           const float* slopes, int causal, hipStream_t stream) {
+  int st = check_common(q, k, k, w, slopes, B, H, N, d, 4);
+  if (st != ALIBI_OK) return st;
+  if (causal != 0 && causal != 1) return ALIBI_EINVAL;
+  if (N > 1024 || d > 256) return ALIBI_ENOTSUP;
+  return hip_status(alibi::launch_weights_f32(q, k, w, B, H, N, d, slopes, causal, scale_log2(d), stream));
+}
+
+const char* alibi_status_string(int status) {
+  switch (status) {
+    case ALIBI_OK: return "ALIBI_OK: success";
+    case ALIBI_EINVAL: return "ALIBI_EINVAL: invalid argument (size, null or misaligned pointer)";
+    case ALIBI_ENOTSUP: return "ALIBI_ENOTSUP: request not supported by this build";
+    case ALIBI_EHIP: return "ALIBI_EHIP: HIP runtime or launch failure";
+    case ALIBI_ENOMEM: return "ALIBI_ENOMEM: decode workspace allocation failed";
+    default: return "ALIBI: unknown status";
+  }
+}
+
+int alibi_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int st = ALIBI_OK;
+  int cur = 0;
+  if (!g_ws.empty() && hipGetDevice(&cur) != hipSuccess) return ALIBI_EHIP;
+  for (size_t dev = 0; dev < g_ws.size(); ++dev) {
+    if (!g_ws[dev].ptr) continue;
+    if (hipSetDevice(int(dev)) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+        hipFree(g_ws[dev].ptr) != hipSuccess)
+      st = ALIBI_EHIP;
+    g_ws[dev].ptr = nullptr;
+    g_ws[dev].bytes = 0;
+  }
+  if (!g_ws.empty()) (void)hipSetDevice(cur);
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Host-side launchers of the device kernels (internal to the library; the
+// public C ABI is include/alibi.h). Each returns hipGetLastError() after the
+// launch. Callers have validated every size and pointer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace alibi {
+
+hipError_t launch_fwd_generic_f32(const float* q, const float* k, const float* v, float* out,
+                                  int B, int H, int N, int d, const float* slopes, int causal,
+                                  float c1, hipStream_t stream);
+hipError_t launch_fwd_generic_bf16(const void* q, const void* k, const void* v, void* out,
+                                   int B, int H, int N, int d, const float* slopes, int causal,
+                                   float c1, hipStream_t stream);
+hipError_t launch_weights_f32(const float* q, const float* k, float* w, int B, int H, int N, int d,
+                              const float* slopes, int causal, float c1, hipStream_t stream);
+
+// MFMA forward, bf16, d in {64, 128}.
+hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, void* out,
+                           int B, int H, int N, int d, const float* slopes, int causal,
+                           float c1, hipStream_t stream);
+
+// Split-KV decode. `splits` key ranges of `chunk` keys each; ws holds
+// B*H*splits*(d+2) floats when splits > 1 (may be null when splits == 1).
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* out, float* ws,
+                         int B, int H, int L, int d, int splits, int chunk,
+                         const float* slopes, float c1, hipStream_t stream);
+
+// Number of splits and keys per split the decode launcher will use.
+void decode_plan(int B, int H, int L, int d, int* splits, int* chunk);
+
+}  // namespace alibi

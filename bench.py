@@ -1,0 +1,176 @@
+#!/usr/bin/env python3
+"""Benchmark of the ALiBi attention hot path on one MI355X.
+
+One step = one pass over both hot-path kernels on resident inputs:
+  * the fused causal ALiBi forward, bf16, B=8 H=16 N=4096 d=128 (the N=4096,
+    d=128 performance shape), and
+  * the split-KV decode, bf16, B=32 H=32 L=32768 d=128.
+`value` is the forward's TFLOP/s (algorithmic causal flops including the
+diagonal, 4 d B H N (N+1) / 2, divided by the forward's own HIP-event time over
+the timed steps); the decode's GB/s (K + V + q + out bytes over its own event
+time) is reported under "decode". Both carry a roofline object against the
+MI355X datasheet peaks (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).
+
+The CPU baseline is the fp64 oracle itself, timed on this host's cores on a
+bounded sample (whole heads of the same forward, whole (b, h) pairs of the
+same decode), scaled to the same units.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def fwd_flops(B, H, N, d):
+    return 4.0 * d * B * H * N * (N + 1) / 2.0
+
+
+def decode_bytes(B, H, L, d):
+    return 2.0 * B * H * L * d * 2 + 2.0 * B * H * d * 2
+
+
+def cpu_baseline(q, k, v, kc, vc, qd, fwd_wl, dec_wl, budget_s=12.0):
+    """Time the oracle on whole heads / (b, h) pairs of the bench workloads."""
+    import numpy as np
+    import torch
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    s_f = oracle.slopes_ref(fwd_wl.H)
+    heads = 0
+    t_f = 0.0
+    while t_f < budget_s and heads < fwd_wl.B * fwd_wl.H:
+        b, h = divmod(heads, fwd_wl.H)
+        qq, kk, vv = (x[b, h].to(torch.float64).numpy() for x in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.attn_head_ref(qq, kk, vv, float(s_f[h]), causal=True)
+        t_f += time.perf_counter() - t0
+        heads += 1
+    fwd_rate = fwd_flops(1, heads, fwd_wl.N, fwd_wl.d) / t_f / 1e12
+    s_d = oracle.slopes_ref(dec_wl.H)
+    pairs = 0
+    t_d = 0.0
+    while t_d < budget_s / 2 and pairs < dec_wl.B * dec_wl.H:
+        b, h = divmod(pairs, dec_wl.H)
+        qq = qd[b:b + 1, h:h + 1].cpu()
+        kk = kc[b:b + 1, h:h + 1].cpu()
+        vv = vc[b:b + 1, h:h + 1].cpu()
+        t0 = time.perf_counter()
+        oracle.decode_ref(qq, kk, vv, s_d[h:h + 1])
+        t_d += time.perf_counter() - t0
+        pairs += 1
+    dec_rate = decode_bytes(1, pairs, dec_wl.L, dec_wl.d) / t_d / 1e9
+    return {
+        "value": fwd_rate, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{heads} of {fwd_wl.B * fwd_wl.H} (b,h) heads of the N={fwd_wl.N} d={fwd_wl.d} "
+                  f"causal forward, fp64 numpy, {t_f:.1f} s",
+        "decode": {"value": dec_rate, "unit": "GB/s",
+                   "sample": f"{pairs} of {dec_wl.B * dec_wl.H} (b,h) pairs of the L={dec_wl.L} decode, "
+                             f"{t_d:.1f} s (host copies excluded)"},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import alibi_linear_position_amd as alibi
+    import workloads as W
+
+    alibi.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fw = W.FWD_B8_H16_N4096_D128
+    dw = W.DECODE_B32_H32_L32768_D128
+
+    q, k, v = W.gaussian_qkv_bf16(fw.shape, seed=fw.seed)
+    qg, kg, vg = (x.to(dev) for x in (q, k, v))
+    out = torch.empty_like(qg)
+    s_f = alibi.slopes(fw.H).to(dev)
+    kc = W.device_gaussian_bf16((dw.B, dw.H, dw.L, dw.d), seed=dw.seed)
+    vc = W.device_gaussian_bf16((dw.B, dw.H, dw.L, dw.d), seed=dw.seed + 1)
+    qd = W.device_gaussian_bf16((dw.B, dw.H, dw.d), seed=dw.seed + 2)
+    od = torch.empty_like(qd)
+    s_d = alibi.slopes(dw.H).to(dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        alibi.attn_fwd(qg, kg, vg, s_f, causal=True, out=out)
+        if ev is not None:
+            ev[1].record()
+        alibi.attn_decode(qd, kc, vc, s_d, out=od)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps / 1e3  # s per launch
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps / 1e3
+    flops = fwd_flops(fw.B, fw.H, fw.N, fw.d)
+    nbytes = decode_bytes(dw.B, dw.H, dw.L, dw.d)
+    tflops = flops / t_fwd / 1e12
+    gbs = nbytes / t_dec / 1e9
+    assert torch.isfinite(out.float()).all() and torch.isfinite(od.float()).all()
+
+    res = {
+        "metric": "causal ALiBi attn fwd TFLOP/s (bf16) + decode HBM GB/s, 1xMI355X",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{fw.name} + {dw.name}", "fwd": {"B": fw.B, "H": fw.H, "N": fw.N, "d": fw.d,
+                                                                "causal": True},
+                   "decode": {"B": dw.B, "H": dw.H, "L": dw.L, "d": dw.d}},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "fwd_mfma_kernel<128,64,1,true>", "ms_per_launch": round(t_fwd * 1e3, 4),
+                     "per_launch": f"{flops:.4e} flop"},
+        "decode": {"value": round(gbs, 1), "unit": "GB/s",
+                   "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                "kernel": "decode_split_kernel<16>", "ms_per_launch": round(t_dec * 1e3, 4),
+                                "per_launch": f"{nbytes:.4e} B"}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(q, k, v, kc, vc, qd, fw, dw)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

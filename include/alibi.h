@@ -1,0 +1,133 @@
+/*
+ * alibi.h -- C ABI of the MI355X (gfx950) causal ALiBi attention library.
+ *
+ * What is computed (per batch b, head h, query i, key j):
+ *   score(i, j) = q_i . k_j / sqrt(d) - m_h * (i - j)      for j <= i
+ *   score(i, j) = -inf                                     for j >  i (causal mask)
+ *   w(i, .)     = softmax over keys of score(i, .)
+ *   out_i       = sum_j w(i, j) v_j
+ * Sources: "When Attention Goes Blind: Numerical Failure in ALiBi Positional
+ * Encodings" (arXiv 2608.03994), Sec. 3.1, Eq. 1-3, and Sec. 3.2, Eq. 4;
+ * "ALiBi: Attention with Linear Biases" (abhik.ai), section "From distance to
+ * a normalized weight". The bias is generated inside the kernels' tiles; no
+ * (H, N, N) bias tensor is ever stored (abhik.ai, remark after the
+ * full-sequence example).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Return value: ALIBI_OK (0) or a negative alibi_status. No exception or
+ *   abort crosses the ABI. Arguments are validated before anything is enqueued;
+ *   on an error nothing is launched and outputs are untouched.
+ * - Device pointers (q, k, v, out, caches, slopes on the attention calls) are
+ *   caller-owned HIP device allocations on the current device. The library
+ *   keeps no pointer past the call's stream order.
+ * - Tensors are dense and contiguous, row-major, head dimension fastest:
+ *   (B, H, N, d) for q/k/v/out, (B, H, L, d) for KV caches, (B, H, d) for the
+ *   decode query and output. Every data pointer must be 16-byte aligned.
+ * - `slopes` holds H fp32 values, one per head, for the GLOBAL head index
+ *   (normally the output of alibi_slopes copied to the device). The library
+ *   cannot detect a mismatched schedule.
+ * - Work is enqueued asynchronously on `stream` (0 = the null stream). A
+ *   launch failure is reported as ALIBI_EHIP; faults inside a kernel surface
+ *   at the caller's next synchronisation.
+ * - Sizes: B, H, N (or L), d >= 1 and N, L <= 2^24 (token distances stay
+ *   exact in fp32). Element offsets are computed in 64-bit.
+ */
+#ifndef ALIBI_H_
+#define ALIBI_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum alibi_status {
+  ALIBI_OK = 0,
+  ALIBI_EINVAL = -1,   /* bad size, null or misaligned pointer */
+  ALIBI_ENOTSUP = -2,  /* valid request this build does not handle (e.g. d > 256) */
+  ALIBI_EHIP = -3,     /* a HIP runtime call or kernel launch failed */
+  ALIBI_ENOMEM = -4    /* the library could not allocate its decode workspace */
+} alibi_status;
+
+/*
+ * Per-head slopes (host only; no device work).
+ * Power-of-two H: m_h = 2^(-8 (h + 1) / H), h = 0 .. H-1. Other H: the
+ * schedule of c = the largest power of two below H, followed by entries
+ * 0, 2, 4, ... of the schedule for 2c until H slopes are listed, in that
+ * order (abhik.ai, "Different heads, different distance penalties"; dev.to
+ * "ALiBi: give a Transformer position sense with one line", "Per-head slopes
+ * form a geometric ladder"). Each power is evaluated in double and rounded
+ * to nearest-even fp32.
+ * slopes_out: caller-owned HOST array of at least H floats.
+ * Errors: H < 1 or slopes_out == NULL -> ALIBI_EINVAL.
+ */
+int alibi_slopes(int H, float* slopes_out);
+
+/*
+ * Fused multi-head ALiBi attention forward, bf16 in / bf16 out, fp32
+ * accumulation and fp32 online softmax.
+ * q, k, v, out: device, bf16, (B, H, N, d) contiguous. out may not alias q/k/v.
+ * slopes: device, H fp32.
+ * causal = 1: the causal form above (Eq. 2-3 of "When Attention Goes Blind").
+ * causal = 0: no mask and the symmetric bias -m_h |i - j| ("ALiBi and Relative
+ *   Position Bias", quantmemo.com, "The mechanics").
+ * d in {64, 128} runs the MFMA kernel; other d that are multiples of 8 up to
+ * 256 run a slower generic kernel. Errors: ALIBI_EINVAL for bad sizes,
+ * pointers or causal not in {0, 1}; ALIBI_ENOTSUP for d > 256 or d % 8 != 0.
+ */
+int alibi_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                   int B, int H, int N, int d, const float* slopes, int causal,
+                   hipStream_t stream);
+
+/*
+ * Same operation in fp32 (inputs, output and all arithmetic), for any
+ * 1 <= d <= 256 (pointers need only 4-byte alignment). Generic kernel; meant
+ * for small and exact checks such as the 4-head, 8-token, d = 16 example of
+ * "ALiBi in Attention: Complete Implementation" (mbrenndoerfer.com).
+ */
+int alibi_attn_fwd_f32(const float* q, const float* k, const float* v, float* out,
+                       int B, int H, int N, int d, const float* slopes, int causal,
+                       hipStream_t stream);
+
+/*
+ * Single-query decode against a KV cache, bf16 in / bf16 out.
+ * q, out: device bf16 (B, H, d); kcache, vcache: device bf16 (B, H, L, d).
+ * The query is the newest token at position L - 1 and key j keeps its real
+ * position j, so the bias is -m_h (L - 1 - j) and every cached key is allowed
+ * (abhik.ai, KV-cache remark after the full-sequence example).
+ * The key range is split across workgroups; partial softmax states are merged
+ * by a second kernel through a library-owned per-device workspace (see
+ * alibi_release). Errors: as alibi_attn_fwd; ALIBI_ENOMEM if the workspace
+ * cannot be allocated. Calls on one device are serialised by a mutex while
+ * they size the workspace; the work itself stays asynchronous.
+ */
+int alibi_attn_decode(const void* q, const void* kcache, const void* vcache, void* out,
+                      int B, int H, int L, int d, const float* slopes,
+                      hipStream_t stream);
+
+/*
+ * TEST ONLY, not on the hot path: materialises the fp32 attention weights
+ * w (B, H, N, N) of the fp32 forward, so the printed weight matrices of the
+ * 4-head seed-42 example can be checked on the device. Masked weights are
+ * written as exact zeros. Rejects N > 1024 (ALIBI_ENOTSUP) and d > 256.
+ */
+int alibi_attn_weights_f32(const float* q, const float* k, float* w,
+                           int B, int H, int N, int d, const float* slopes, int causal,
+                           hipStream_t stream);
+
+/* Static, never-NULL description of a status code. */
+const char* alibi_status_string(int status);
+
+/*
+ * Frees the library-owned decode workspaces on every device after a device
+ * synchronisation. Safe to call at any time; later decode calls re-allocate.
+ */
+int alibi_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ALIBI_H_ */

@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* libalibi.so loads and exports every function include/alibi.h declares.
+* alibi_slopes (host code) is bitwise equal to the oracle's slopes.
+* Every argument error is reported before anything would be enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "alibi.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import alibi_linear_position_amd as alibi
+    return alibi.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(alibi_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("alibi_slopes", "alibi_attn_fwd", "alibi_attn_decode", "alibi_attn_fwd_f32",
+              "alibi_attn_weights_f32", "alibi_status_string", "alibi_release"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import alibi_linear_position_amd as alibi
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert name in alibi.EXPORTS, name
+
+
+@pytest.mark.parametrize("H", list(range(1, 131)) + [256, 1000])
+def test_host_slopes_bitwise_equal_oracle(H):
+    import alibi_linear_position_amd as alibi
+    got = alibi.slopes(H).numpy()
+    want = oracle.slopes_ref(H)
+    assert got.dtype == np.float32
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_slopes_no_double_rounding_hazard():
+    # the fp64 power must not sit within 1 ulp of an fp32 rounding midpoint,
+    # or two correctly rounded doubles could round to different floats
+    for H in list(range(1, 131)) + [256]:
+        c = 1 << (H.bit_length() - 1)
+        exps = [-8.0 * (h + 1) / c for h in range(c)] + [-8.0 * (2 * t + 1) / (2 * c) for t in range(H - c)]
+        for e in exps:
+            x = 2.0 ** e
+            f = np.float32(x)
+            if float(f) == x:
+                continue
+            lo, hi = (np.nextafter(f, np.float32(0)), f) if float(f) > x else (f, np.nextafter(f, np.float32(1)))
+            mid = (float(lo) + float(hi)) / 2
+            assert abs(x - mid) > 2 * np.spacing(x), (H, e)
+
+
+def test_slopes_errors(lib):
+    buf = (ctypes.c_float * 4)()
+    assert lib.alibi_slopes(0, buf) == -1
+    assert lib.alibi_slopes(-3, buf) == -1
+    assert lib.alibi_slopes(4, None) == -1
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, 7):
+        s = lib.alibi_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.alibi_status_string(-1).startswith(b"ALIBI_EINVAL")
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, fn="alibi_attn_fwd", q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=1, N=8, d=64, s=FAKE, causal=1):
+    return getattr(lib, fn)(q, k, v, o, B, H, N, d, s, causal, None)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, q=None) == -1
+    assert _fwd(lib, k=None) == -1
+    assert _fwd(lib, v=None) == -1
+    assert _fwd(lib, o=None) == -1
+    assert _fwd(lib, s=None) == -1
+    for bad in (dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(N=(1 << 24) + 1), dict(B=-1)):
+        assert _fwd(lib, **bad) == -1, bad
+    assert _fwd(lib, q=FAKE + 8) == -1     # bf16 path needs 16-byte alignment
+    assert _fwd(lib, o=FAKE + 2) == -1
+    assert _fwd(lib, s=FAKE + 2) == -1     # slopes need 4-byte alignment
+    assert _fwd(lib, causal=2) == -1
+    assert _fwd(lib, d=264) == -2          # beyond 256
+    assert _fwd(lib, d=60) == -2           # not a multiple of 8 on the bf16 path
+
+
+def test_fwd_f32_validation(lib):
+    assert _fwd(lib, "alibi_attn_fwd_f32", q=None, d=16) == -1
+    assert _fwd(lib, "alibi_attn_fwd_f32", N=0, d=16) == -1
+    assert _fwd(lib, "alibi_attn_fwd_f32", d=300) == -2
+    assert _fwd(lib, "alibi_attn_fwd_f32", causal=-1, d=16) == -1
+    assert _fwd(lib, "alibi_attn_fwd_f32", q=FAKE + 2, d=16) == -1
+
+
+def test_decode_validation(lib):
+    f = lib.alibi_attn_decode
+    assert f(None, FAKE, FAKE, FAKE, 1, 1, 8, 128, FAKE, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 0, 128, FAKE, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 127, FAKE, None) == -2
+    assert f(FAKE, FAKE + 4, FAKE, FAKE, 1, 1, 8, 128, FAKE, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 128, None, None) == -1
+
+
+def test_weights_validation(lib):
+    f = lib.alibi_attn_weights_f32
+    assert f(FAKE, FAKE, FAKE, 1, 1, 1025, 16, FAKE, 1, None) == -2
+    assert f(None, FAKE, FAKE, 1, 1, 8, 16, FAKE, 1, None) == -1
+    assert f(FAKE, FAKE, FAKE, 1, 1, 8, 16, FAKE, 3, None) == -1
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    import alibi_linear_position_amd as alibi
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        alibi.attn_fwd(x, x, x)
+    with pytest.raises(ValueError):
+        alibi.attn_decode(x[:, :, 0], x, x)
