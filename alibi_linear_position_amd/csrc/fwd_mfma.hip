@@ -11,10 +11,10 @@
 //
 // Layout of the work
 // ------------------
-// * A workgroup is NW waves (8 by default) and owns BM = 32 NW consecutive
+// * A workgroup is NW waves (4 by default) and owns BM = 32 NW consecutive
 //   query rows of one (b, h); each wave owns 32 rows. Two waves share each SIMD
-//   (at most 256 registers per lane), so one wave's MFMA work overlaps the
-//   other's softmax arithmetic.
+//   (at most 256 registers per lane; two 4-wave workgroups per CU), so one
+//   wave's MFMA work can overlap the other's softmax arithmetic.
 // * Key/value tiles of BN = 64 rows are staged HBM -> registers -> LDS by the
 //   whole workgroup: K row-major (16-byte coalesced loads, rows padded by 16 B
 //   against bank conflicts), V transposed to V^T[d][key] (one key per lane,
@@ -39,8 +39,10 @@
 //   Off-diagonal tiles use a cheap upper bound of the row maximum
 //   (max_j s_ij * c1 plus the largest bias in the tile) instead of the exact
 //   maximum; any bound works for the algebra and this one keeps p <= 2^8.
-//   There the bias costs one add (with a wave-uniform offset held in a scalar
-//   register) and one fma per score.
+//   The first Q K^T k-step takes a constant register set as its C operand,
+//   which seeds each score with its register's bias offset, so there the bias
+//   costs one fma per score. Row reductions across the two lane halves use
+//   v_permlane32_swap; row sums use four independent accumulators.
 // * The row sum is accumulated from the bf16-rounded p that the PV product
 //   uses (v_dot2c_f32_bf16), so the normalisation matches the numerator.
 // * Grid: one workgroup per (b, h, query block), heaviest causal blocks first
@@ -55,11 +57,12 @@ namespace alibi {
 
 namespace {
 
-// Waves per workgroup: 8 by default; ALIBI_FWD_NW=4 selects 4 (tuning only).
+// Waves per workgroup: 4 by default (two workgroups share a CU);
+// ALIBI_FWD_NW=8 selects one 8-wave workgroup per CU (tuning only).
 int fwd_waves() {
   static const int nw = [] {
     const char* e = std::getenv("ALIBI_FWD_NW");
-    return (e != nullptr && std::atoi(e) == 4) ? 4 : 8;
+    return (e != nullptr && std::atoi(e) == 8) ? 8 : 4;
   }();
   return nw;
 }
@@ -71,6 +74,27 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 // Position of key x (0..15) inside a 16-key group of V^T: swaps keys 4-7 with 8-11.
 __device__ __forceinline__ int perm16(int x) { return ((x & 4) << 1) | ((x & 8) >> 1) | (x & 3); }
+
+// Row reductions across the two lane halves (lane l and l ^ 32 hold the same
+// query): v_permlane32_swap exchanges the halves in one VALU op.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum of 16 accumulator values as a shallow tree of 3-input maxima.
+__device__ __forceinline__ float max16(const f32x16& a) {
+  const float m0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  const float m1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  const float m2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
+  const float m3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
+  const float m4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
+  return fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), a[15]));
+}
 
 __device__ __forceinline__ float bdot2(uint32_t packed, float acc) {
   const bf16x2 a = __builtin_bit_cast(bf16x2, packed);
@@ -164,15 +188,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   const int qw_last = min(qw0 + 32, N) - 1;            // last valid query of this wave
   const int i = qw0 + l32;                             // this lane's query
 
-  // Bias offsets m log2(e) (32 kb + 8 g + r) of the accumulator registers: wave-uniform,
-  // kept in scalar registers.
-  float cr[KB][16];
+  // C operand of the first Q K^T k-step: seeds register r of a 32-key block
+  // with its bias offset m log2(e) (8 (r / 4) + r % 4) / c1, so off-diagonal
+  // tiles need one fma per score to complete the bias.
+  f32x16 cinit;
+  const float c21 = c2 / c1;
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      cr[kb][r] = __int_as_float(__builtin_amdgcn_readfirstlane(
-          __float_as_int(c2 * float(32 * kb + 8 * (r >> 2) + (r & 3)))));
+  for (int r = 0; r < 16; ++r) cinit[r] = c21 * float(8 * (r >> 2) + (r & 3));
 
   // Q^T fragments (MFMA B operand): lane holds query l32, d = 16 ks + 8 hi .. +7.
   bf16x8 qf[KS];
@@ -209,27 +231,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       // ---- S^T = K Q^T ----
       f32x16 s[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
-          s[kb] = mfma32(a, qf[ks], s[kb]);
+          s[kb] = mfma32(a, qf[ks], ks == 0 ? cinit : s[kb]);
         }
       }
 
       // ---- bias, mask, online softmax ----
       const bool fast = CAUSAL && (j0 + BN - 1 <= qw0) && (j0 + BN <= N);
       float mcand;
+      // s = q.k + (c2 / c1)(8 (r / 4) + r % 4); the full exponent is
+      // t = s c1 + c2 (j0 + 32 kb + 4 hi - i).
+      const float bt0 = c2 * float(j0 + 4 * hi - i);
+      const float bt1 = bt0 + 32.0f * c2;
       if (fast) {
-        float smax = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[kb][r]);
-        smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-        mcand = fmaf(smax, c1, c2 * float(j0 + BN - 1 - i));
+        mcand = max_xor32(fmaxf(fmaf(max16(s[0]), c1, bt0), fmaf(max16(s[1]), c1, bt1)));
       } else {
         float tmax = kNegInf;
 #pragma unroll
@@ -238,13 +256,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
           for (int r = 0; r < 16; ++r) {
             const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
             const bool valid = j < N && (!CAUSAL || j <= i);
-            const float dist = float(i - j);
-            const float t = fmaf(s[kb][r], c1, -c2 * fabsf(dist));
+            float t = fmaf(s[kb][r], c1, kb ? bt1 : bt0);
+            if (!CAUSAL && j > i) t -= 2.0f * c2 * float(j - i);  // symmetric bias -m |i - j|
             s[kb][r] = valid ? t : kNegInf;  // now holds t (log2 units)
             tmax = fmaxf(tmax, s[kb][r]);
           }
         }
-        mcand = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        mcand = max_xor32(tmax);
       }
       const bool need = mcand > m_run + kLazy;
       if (__builtin_amdgcn_ballot_w64(need)) {
@@ -257,9 +275,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       }
       const float m_use = m_run == kNegInf ? 0.0f : m_run;
       u32x4 pf[PS];
-      float lsum = l_run;
+      float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
       if (fast) {
-        const float bt = fmaf(c2, float(j0 + 4 * hi - i), -m_use);
+        const float b0 = bt0 - m_use, b1 = bt1 - m_use;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -268,10 +286,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r0 = 8 * half + 2 * e;
-              const float p0 = fast_exp2(fmaf(s[kb][r0], c1, bt + cr[kb][r0]));
-              const float p1 = fast_exp2(fmaf(s[kb][r0 + 1], c1, bt + cr[kb][r0 + 1]));
-              pk[e] = pack_bf16x2(p0, p1);
-              lsum = bdot2(pk[e], lsum);
+              const float bb = kb ? b1 : b0;
+              pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], c1, bb)), fast_exp2(fmaf(s[kb][r0 + 1], c1, bb)));
+              lpart[e] = bdot2(pk[e], lpart[e]);
             }
             pf[2 * kb + half] = pk;
           }
@@ -286,13 +303,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
             for (int e = 0; e < 4; ++e) {
               const int r0 = 8 * half + 2 * e;
               pk[e] = pack_bf16x2(fast_exp2(s[kb][r0] - m_use), fast_exp2(s[kb][r0 + 1] - m_use));
-              lsum = bdot2(pk[e], lsum);
+              lpart[e] = bdot2(pk[e], lpart[e]);
             }
             pf[2 * kb + half] = pk;
           }
         }
       }
-      l_run = lsum;
+      l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
 
       // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -308,7 +325,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   }
 
   // ---- epilogue: O / l -> bf16 ----
-  const float lt = l_run + __shfl_xor(l_run, 32, 64);
+  const float lt = sum_xor32(l_run);
   const float inv = 1.0f / lt;
   if (i < N) {
 #pragma unroll

@@ -16,6 +16,11 @@ bounded sample (whole heads of the same forward, whole (b, h) pairs of the
 same decode), scaled to the same units.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --only fwd|decode|copy [--steps K] [--warmup W]
+
+`--only` runs a single kernel (or, for `copy`, a plain device-to-device copy of
+a 1 GiB bf16 tensor) so that hardware-counter runs see one kernel; it prints a
+short JSON line and no CPU baseline. The copy calibrates the HBM byte counters.
 """
 import argparse
 import json
@@ -37,6 +42,29 @@ def fwd_flops(B, H, N, d):
 
 def decode_bytes(B, H, L, d):
     return 2.0 * B * H * L * d * 2 + 2.0 * B * H * d * 2
+
+
+def traffic_bytes(profile_md, sources):
+    """HBM bytes per launch from a committed counter summary, or None.
+
+    The summary under profiles/ carries a `traffic_record` line with the kernel
+    source hash it was measured on; a changed kernel gets None.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile_md)
+    try:
+        rec = None
+        for line in open(path):
+            if line.strip().startswith("traffic_record:"):
+                rec = json.loads(line.split("traffic_record:", 1)[1])
+        if rec is None:
+            return None
+        h = hashlib.sha256()
+        for f in sources:
+            h.update(open(os.path.join(ROOT, "alibi_linear_position_amd", "csrc", f), "rb").read())
+        return rec["traffic_bytes"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def cpu_baseline(q, k, v, kc, vc, qd, fwd_wl, dec_wl, budget_s=12.0):
@@ -85,6 +113,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -100,6 +129,8 @@ def main():
     torch.cuda.set_device(dev)
     fw = W.FWD_B8_H16_N4096_D128
     dw = W.DECODE_B32_H32_L32768_D128
+    if args.only is not None:
+        return run_only(args, alibi, W, fw, dw, dev)
 
     q, k, v = W.gaussian_qkv_bf16(fw.shape, seed=fw.seed)
     qg, kg, vg = (x.to(dev) for x in (q, k, v))
@@ -157,12 +188,15 @@ def main():
                                                                 "causal": True},
                    "decode": {"B": dw.B, "H": dw.H, "L": dw.L, "d": dw.d}},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fwd_mfma_kernel<128,64,1,true>", "ms_per_launch": round(t_fwd * 1e3, 4),
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_bytes("fwd_mfma_B8_H16_N4096_d128.md", ["fwd_mfma.hip", "device_common.h"]),
+                     "kernel": f"fwd_mfma_kernel<128,{os.environ.get('ALIBI_FWD_NW', '4')},true>", "ms_per_launch": round(t_fwd * 1e3, 4),
                      "per_launch": f"{flops:.4e} flop"},
         "decode": {"value": round(gbs, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                "traffic": traffic_bytes("decode_split_B32_H32_L32768_d128.md",
+                                                         ["decode.hip", "device_common.h"]),
                                 "kernel": "decode_split_kernel<16>", "ms_per_launch": round(t_dec * 1e3, 4),
                                 "per_launch": f"{nbytes:.4e} B"}},
         "cpu_baseline": None,
@@ -170,6 +204,42 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(q, k, v, kc, vc, qd, fw, dw)
     print(json.dumps(res), flush=True)
+
+
+def run_only(args, alibi, W, fw, dw, dev):
+    """One kernel, W + K launches, HIP-event timed; for counter runs."""
+    import torch
+    if args.only == "fwd":
+        q, k, v = (x.to(dev) for x in W.gaussian_qkv_bf16(fw.shape, seed=fw.seed))
+        out = torch.empty_like(q)
+        s = alibi.slopes(fw.H).to(dev)
+        fn = lambda: alibi.attn_fwd(q, k, v, s, causal=True, out=out)
+        work, unit = fwd_flops(fw.B, fw.H, fw.N, fw.d), "flop"
+    elif args.only == "decode":
+        kc = W.device_gaussian_bf16((dw.B, dw.H, dw.L, dw.d), seed=dw.seed)
+        vc = W.device_gaussian_bf16((dw.B, dw.H, dw.L, dw.d), seed=dw.seed + 1)
+        qd = W.device_gaussian_bf16((dw.B, dw.H, dw.d), seed=dw.seed + 2)
+        od = torch.empty_like(qd)
+        s = alibi.slopes(dw.H).to(dev)
+        fn = lambda: alibi.attn_decode(qd, kc, vc, s, out=od)
+        work, unit = decode_bytes(dw.B, dw.H, dw.L, dw.d), "B"
+    else:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)
+        work, unit = 2.0 * src.numel() * 2, "B (read + write)"
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"only": args.only, "ms_per_launch": round(ms, 4), "work_per_launch": work,
+                      "unit": unit, "rate": work / ms / 1e9}), flush=True)
 
 
 if __name__ == "__main__":
