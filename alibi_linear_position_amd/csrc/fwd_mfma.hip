@@ -311,7 +311,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       }
       l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
 
-      // ---- O^T += V^T P^T ----
+      // ---- O^T += V^T P^T, with the next tile's LDS stores in the same region ----
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -320,8 +320,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
           o[db] = mfma32(a, __builtin_bit_cast(bf16x8, pf[ps]), o[db]);
         }
       }
+      // After the last tile the registers still hold tile 0, which nobody reads
+      // again; storing it keeps this region free of branches.
+      regs.template store<KPITCH, VPITCH>(smem + (stage ^ 1) * STAGE, smem + (stage ^ 1) * STAGE + KBYTES, tid);
+    } else {
+      regs.template store<KPITCH, VPITCH>(smem + (stage ^ 1) * STAGE, smem + (stage ^ 1) * STAGE + KBYTES, tid);
     }
-    if (tile > 0) regs.template store<KPITCH, VPITCH>(smem + (stage ^ 1) * STAGE, smem + (stage ^ 1) * STAGE + KBYTES, tid);
   }
 
   // ---- epilogue: O / l -> bf16 ----

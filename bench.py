@@ -44,14 +44,14 @@ def decode_bytes(B, H, L, d):
     return 2.0 * B * H * L * d * 2 + 2.0 * B * H * d * 2
 
 
-def traffic_bytes(profile_md, sources):
+def traffic_bytes(profile_md, sources, root=ROOT):
     """HBM bytes per launch from a committed counter summary, or None.
 
     The summary under profiles/ carries a `traffic_record` line with the kernel
     source hash it was measured on; a changed kernel gets None.
     """
     import hashlib
-    path = os.path.join(ROOT, "profiles", profile_md)
+    path = os.path.join(root, "profiles", profile_md)
     try:
         rec = None
         for line in open(path):
@@ -61,7 +61,7 @@ def traffic_bytes(profile_md, sources):
             return None
         h = hashlib.sha256()
         for f in sources:
-            h.update(open(os.path.join(ROOT, "alibi_linear_position_amd", "csrc", f), "rb").read())
+            h.update(open(os.path.join(root, "alibi_linear_position_amd", "csrc", f), "rb").read())
         return rec["traffic_bytes"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
     except (OSError, ValueError, KeyError):
         return None

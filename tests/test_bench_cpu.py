@@ -13,15 +13,22 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in r.stderr
 
 
-def test_traffic_record_is_hash_guarded(tmp_path, monkeypatch):
+def test_traffic_record_is_hash_guarded(tmp_path):
+    import hashlib
+    import json
     sys.path.insert(0, ROOT)
     import bench
-    # the committed records match the committed kernel sources
-    assert bench.traffic_bytes("fwd_mfma_B8_H16_N4096_d128.md", ["fwd_mfma.hip", "device_common.h"]) > 0
-    assert bench.traffic_bytes("decode_split_B32_H32_L32768_d128.md", ["decode.hip", "device_common.h"]) > 0
-    # a record measured on other sources is ignored
-    assert bench.traffic_bytes("fwd_mfma_B8_H16_N4096_d128.md", ["decode.hip"]) is None
-    assert bench.traffic_bytes("no_such_file.md", ["decode.hip"]) is None
+    csrc = tmp_path / "alibi_linear_position_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    (csrc / "k.hip").write_bytes(b"kernel v1")
+    digest = hashlib.sha256(b"kernel v1").hexdigest()[:16]
+    rec = {"source_sha256_16": digest, "traffic_bytes": 1234}
+    (tmp_path / "profiles" / "k.md").write_text("# k\n\n    traffic_record: " + json.dumps(rec) + "\n")
+    assert bench.traffic_bytes("k.md", ["k.hip"], root=str(tmp_path)) == 1234
+    (csrc / "k.hip").write_bytes(b"kernel v2")  # the kernel changed since the counters were taken
+    assert bench.traffic_bytes("k.md", ["k.hip"], root=str(tmp_path)) is None
+    assert bench.traffic_bytes("missing.md", ["k.hip"], root=str(tmp_path)) is None
 
 
 def test_flop_and_byte_conventions():
