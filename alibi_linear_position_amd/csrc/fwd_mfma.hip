@@ -52,6 +52,7 @@
 #include "launch.h"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace alibi {
 
@@ -126,6 +127,21 @@ struct TileRegs {
       const int vcol = tid / BN + (NT / BN) * r;
       v[r] = u32x4{0u, 0u, 0u, 0u};
       if (j0 + key < N) v[r] = *reinterpret_cast<const u32x4*>(vg + base + (long long)(j0 + key) * D + vcol * 8);
+    }
+  }
+
+  // A tile that lies entirely below N: no guards and no zero fill. Chunk r of
+  // K sits at element (tid + NT r) * 8 of the tile (rows are contiguous), chunk
+  // r of V at key * D + (tid / BN + (NT / BN) r) * 8: one per-thread offset
+  // plus a constant per chunk.
+  __device__ __forceinline__ void load_full(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
+                                            int tid) {
+    const uint32_t koff = uint32_t(tid) * 8u;
+    const uint32_t voff = uint32_t(tid % BN) * D + uint32_t(tid / BN) * 8u;
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      k[r] = *reinterpret_cast<const u32x4*>(kt + koff + uint32_t(NT * 8 * r));
+      v[r] = *reinterpret_cast<const u32x4*>(vt + voff + uint32_t((NT / BN) * 8 * r));
     }
   }
 
@@ -217,116 +233,118 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   regs.load(k, v, base, (ntiles - 1) * BN, N, tid);
   regs.template store<KPITCH, VPITCH>(smem, smem + KBYTES, tid);
 
+  // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T, and the LDS stores
+  // of the next tile (whose global loads were issued at the top). MASKED tiles
+  // may hold keys past a query or past N; the others hold none for any wave.
   int stage = 0;
-  for (int tile = ntiles - 1; tile >= 0; --tile, stage ^= 1) {
+  auto step = [&](int tile, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int j0 = tile * BN;
     // Stage `stage` holds this tile; every wave is done with the other stage.
     __syncthreads();
-    if (tile > 0) regs.load(k, v, base, j0 - BN, N, tid);  // in flight during the compute
+    // Only the first tile visited can be ragged, and the prologue staged it.
+    if (tile > 0) regs.load_full(k + base + (long long)(j0 - BN) * D, v + base + (long long)(j0 - BN) * D, tid);
     const unsigned char* sK = smem + stage * STAGE;
     const unsigned char* sV = sK + KBYTES;
-
-    const bool active = qw0 < N && (!CAUSAL || j0 <= qw_last);
-    if (active) {
-      // ---- S^T = K Q^T ----
-      f32x16 s[KB];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
-          s[kb] = mfma32(a, qf[ks], ks == 0 ? cinit : s[kb]);
-        }
-      }
-
-      // ---- bias, mask, online softmax ----
-      const bool fast = CAUSAL && (j0 + BN - 1 <= qw0) && (j0 + BN <= N);
-      float mcand;
-      // s = q.k + (c2 / c1)(8 (r / 4) + r % 4); the full exponent is
-      // t = s c1 + c2 (j0 + 32 kb + 4 hi - i).
-      const float bt0 = c2 * float(j0 + 4 * hi - i);
-      const float bt1 = bt0 + 32.0f * c2;
-      if (fast) {
-        mcand = max_xor32(fmaxf(fmaf(max16(s[0]), c1, bt0), fmaf(max16(s[1]), c1, bt1)));
-      } else {
-        float tmax = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool valid = j < N && (!CAUSAL || j <= i);
-            float t = fmaf(s[kb][r], c1, kb ? bt1 : bt0);
-            if (!CAUSAL && j > i) t -= 2.0f * c2 * float(j - i);  // symmetric bias -m |i - j|
-            s[kb][r] = valid ? t : kNegInf;  // now holds t (log2 units)
-            tmax = fmaxf(tmax, s[kb][r]);
-          }
-        }
-        mcand = max_xor32(tmax);
-      }
-      const bool need = mcand > m_run + kLazy;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mcand : m_run;
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == kNegInf ? 0.0f : m_run;
-      u32x4 pf[PS];
-      float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
-      if (fast) {
-        const float b0 = bt0 - m_use, b1 = bt1 - m_use;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            u32x4 pk;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r0 = 8 * half + 2 * e;
-              const float bb = kb ? b1 : b0;
-              pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], c1, bb)), fast_exp2(fmaf(s[kb][r0 + 1], c1, bb)));
-              lpart[e] = bdot2(pk[e], lpart[e]);
-            }
-            pf[2 * kb + half] = pk;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            u32x4 pk;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r0 = 8 * half + 2 * e;
-              pk[e] = pack_bf16x2(fast_exp2(s[kb][r0] - m_use), fast_exp2(s[kb][r0 + 1] - m_use));
-              lpart[e] = bdot2(pk[e], lpart[e]);
-            }
-            pf[2 * kb + half] = pk;
-          }
-        }
-      }
-      l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
-
-      // ---- O^T += V^T P^T, with the next tile's LDS stores in the same region ----
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + (32 * db + l32) * VPITCH + (16 * ps + 8 * hi) * 2);
-          o[db] = mfma32(a, __builtin_bit_cast(bf16x8, pf[ps]), o[db]);
-        }
-      }
-      // After the last tile the registers still hold tile 0, which nobody reads
-      // again; storing it keeps this region free of branches.
-      regs.template store<KPITCH, VPITCH>(smem + (stage ^ 1) * STAGE, smem + (stage ^ 1) * STAGE + KBYTES, tid);
-    } else {
-      regs.template store<KPITCH, VPITCH>(smem + (stage ^ 1) * STAGE, smem + (stage ^ 1) * STAGE + KBYTES, tid);
+    unsigned char* const sKn = smem + (stage ^ 1) * STAGE;
+    stage ^= 1;
+    if (MASKED && !(qw0 < N && (!CAUSAL || j0 <= qw_last))) {
+      regs.template store<KPITCH, VPITCH>(sKn, sKn + KBYTES, tid);
+      return;
     }
-  }
+
+    // ---- S^T = K Q^T ----
+    f32x16 s[KB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
+        s[kb] = mfma32(a, qf[ks], ks == 0 ? cinit : s[kb]);
+      }
+    }
+
+    // ---- bias, mask, online softmax ----
+    // s = q.k + (c2 / c1)(8 (r / 4) + r % 4); the full exponent is
+    // t = s c1 + c2 (j0 + 32 kb + 4 hi - i).
+    const float bt0 = c2 * float(j0 + 4 * hi - i);
+    const float bt1 = bt0 + 32.0f * c2;
+    float mcand;
+    if (!MASKED) {
+      // every key is visible: max16 of s bounds the row maximum
+      mcand = max_xor32(fmaxf(fmaf(max16(s[0]), c1, bt0), fmaf(max16(s[1]), c1, bt1)));
+    } else {
+      // masked keys become -inf in s itself, so the exponent code is shared
+      float tmax = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool valid = j < N && (!CAUSAL || j <= i);
+          float x = s[kb][r];
+          if (!CAUSAL && j > i) x -= 2.0f * c21 * float(j - i);  // symmetric bias -m |i - j|
+          s[kb][r] = valid ? x : kNegInf;
+          tmax = fmaxf(tmax, fmaf(s[kb][r], c1, kb ? bt1 : bt0));
+        }
+      }
+      mcand = max_xor32(tmax);
+    }
+    // Lazy rescale: the running maximum moves only when a row's candidate
+    // exceeds it by more than 2^kLazy, so p stays below 2^kLazy.
+    const bool need = mcand > m_run + kLazy;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mcand : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    // m_run is finite after the first visible key; a row with none yet
+    // (every key masked) keeps -inf and takes 0 here
+    const float m_use = MASKED && m_run == kNegInf ? 0.0f : m_run;
+    u32x4 pf[PS];
+    float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
+    const float b0 = bt0 - m_use, b1 = bt1 - m_use;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r0 = 8 * half + 2 * e;
+          const float bb = kb ? b1 : b0;
+          pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], c1, bb)), fast_exp2(fmaf(s[kb][r0 + 1], c1, bb)));
+          lpart[e] = bdot2(pk[e], lpart[e]);
+        }
+        pf[2 * kb + half] = pk;
+      }
+    }
+    l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+
+    // ---- O^T += V^T P^T, with the next tile's LDS stores in the same region ----
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int ps = 0; ps < PS; ++ps) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + (32 * db + l32) * VPITCH + (16 * ps + 8 * hi) * 2);
+        o[db] = mfma32(a, __builtin_bit_cast(bf16x8, pf[ps]), o[db]);
+      }
+    }
+    // After the last tile the registers still hold tile 0, which nobody reads
+    // again; storing it keeps this region free of branches.
+    regs.template store<KPITCH, VPITCH>(sKn, sKn + KBYTES, tid);
+  };
+
+  // Tiles 0 .. t_open lie wholly below the workgroup's first query q0 (so below
+  // every wave's queries, and below N): no mask. The rest, at most
+  // (BM + BN - 1) / BN of them under the causal mask, take the masked path.
+  const int t_open = CAUSAL ? (q0 + 1) / BN - 1 : -1;
+  int tile = ntiles - 1;
+  for (; tile > t_open; --tile) step(tile, std::true_type{});
+  for (; tile >= 0; --tile) step(tile, std::false_type{});
 
   // ---- epilogue: O / l -> bf16 ----
   const float lt = sum_xor32(l_run);
