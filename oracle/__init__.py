@@ -20,3 +20,6 @@ from .underflow import (  # noqa: F401
     underflow_fraction_by_distance, underflow_fraction_causal, underflow_fraction_data,
     log_scaled_blindness_distance,
 )
+from .mitigations import (  # noqa: F401
+    TAU_D, recipe_distances, slopes_recipe_ref, variant_head_ref, variant_ref,
+)
