@@ -8,6 +8,10 @@ or a call returns an error status, these functions raise.
     slopes(H)                          -> float32 CPU tensor (host generator)
     attn_fwd(q, k, v, slopes, causal)  -> bf16 (B, H, N, d)
     attn_fwd_f32(q, k, v, slopes, causal)
+    attn_fwd_ex(q, k, v, slopes, causal, clamp=, log_distance=, softcap=,
+                q_offset=, k_offset=)     -> mitigations / position offsets,
+                                             bf16 or fp32 by q's dtype
+    slopes_recipe(recipe, H, log_distance) -> float32 CPU tensor
     attn_decode(q, kcache, vcache, slopes)  -> bf16 (B, H, d)
     attn_weights_f32(q, k, slopes, causal)  -> fp32 (B, H, N, N), test only
 """
@@ -31,9 +35,23 @@ EXPORTS = {
     "alibi_attn_fwd_f32": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
     "alibi_attn_decode": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
     "alibi_attn_weights_f32": [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
+    "alibi_attn_fwd_ex": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P],
+    "alibi_attn_fwd_ex_f32": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P],
+    "alibi_slopes_recipe": [_I, _I, _I, _P],
     "alibi_status_string": [_I],
     "alibi_release": [],
 }
+
+# mitigation bits of alibi_fwd_opts.flags and the slope recipes (include/alibi.h)
+CLAMP, LOG_DISTANCE, SOFTCAP = 1, 2, 4
+RECIPES = {"default": 0, "steep": 1, "safe": 2, "wide": 3, "explicit": 4}
+
+
+class FwdOpts(ctypes.Structure):
+    """Mirror of struct alibi_fwd_opts."""
+    _fields_ = [("flags", ctypes.c_int), ("clamp_min", ctypes.c_float), ("softcap", ctypes.c_float),
+                ("q_offset", ctypes.c_int), ("k_offset", ctypes.c_int)]
+
 
 _lib = None
 
@@ -75,6 +93,18 @@ def slopes(H: int):
     import torch
     out = torch.empty(int(H), dtype=torch.float32)
     _check("alibi_slopes", load_library().alibi_slopes(int(H), ctypes.c_void_p(out.data_ptr())))
+    return out
+
+
+def slopes_recipe(recipe: str, H: int, log_distance: bool = False):
+    """Slopes from target blindness distances (float32 CPU tensor); see alibi_slopes_recipe."""
+    import torch
+    out = torch.empty(int(H), dtype=torch.float32)
+    if recipe not in RECIPES:
+        raise ValueError(f"unknown recipe {recipe!r}; one of {sorted(RECIPES)}")
+    st = load_library().alibi_slopes_recipe(RECIPES[recipe], int(H), int(bool(log_distance)),
+                                            ctypes.c_void_p(out.data_ptr()))
+    _check("alibi_slopes_recipe", st)
     return out
 
 
@@ -135,6 +165,47 @@ def attn_fwd_f32(q, k, v, slopes=None, causal=True, out=None):
     """fp32 ALiBi attention forward (generic kernel)."""
     import torch
     return _fwd("alibi_attn_fwd_f32", torch.float32, q, k, v, slopes, causal, out)
+
+
+def attn_fwd_ex(q, k, v, slopes=None, causal=True, clamp=None, log_distance=False, softcap=None,
+                q_offset=0, k_offset=0, out=None):
+    """Forward with mitigations and position offsets.
+
+    q: (B, H, Nq, d); k, v: (B, H, Nk, d); bf16 (MFMA / generic kernel) or fp32
+    (generic kernel), by q's dtype. clamp: bias floor or None; log_distance:
+    ln(D + 1) distances; softcap: z or None; query row r sits at position
+    q_offset + r, key row c at k_offset + c.
+    """
+    import torch
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bfloat16 or float32")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, dtype, 4, n)
+    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("expected q (B, H, Nq, d) and k, v (B, H, Nk, d)")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    s = _slopes_dev(slopes, H, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, dtype, 4, "out")
+    o = FwdOpts()
+    o.flags = (CLAMP if clamp is not None else 0) | (LOG_DISTANCE if log_distance else 0) | \
+        (SOFTCAP if softcap is not None else 0)
+    o.clamp_min = float(clamp) if clamp is not None else 0.0
+    o.softcap = float(softcap) if softcap is not None else 0.0
+    o.q_offset = int(q_offset)
+    o.k_offset = int(k_offset)
+    entry = "alibi_attn_fwd_ex" if dtype == torch.bfloat16 else "alibi_attn_fwd_ex_f32"
+    with torch.cuda.device(q.device):
+        st = getattr(load_library(), entry)(
+            _P(q.data_ptr()), _P(k.data_ptr()), _P(v.data_ptr()), _P(out.data_ptr()),
+            B, H, Nq, Nk, d, _P(s.data_ptr()), int(bool(causal)), ctypes.byref(o),
+            _stream_handle(q.device))
+    _check(entry, st)
+    return out
 
 
 def attn_decode(q, kcache, vcache, slopes=None, out=None):

@@ -44,6 +44,32 @@ int check_common(const void* a, const void* b, const void* c, const void* out, c
   return ALIBI_OK;
 }
 
+// Validation of a forward call; fills *opt from opts (NULL = defaults).
+int check_fwd(const void* q, const void* k, const void* v, const void* out, const float* slopes,
+              int B, int H, int Nq, int Nk, int d, int causal, const alibi_fwd_opts* opts,
+              uintptr_t align, alibi::FwdOptions* opt) {
+  int st = check_common(q, k, v, out, slopes, B, H, Nq, d, align);
+  if (st != ALIBI_OK) return st;
+  if (Nk < 1 || Nk > kMaxLen) return ALIBI_EINVAL;
+  if (causal != 0 && causal != 1) return ALIBI_EINVAL;
+  *opt = alibi::FwdOptions{};
+  if (opts != nullptr) {
+    if ((opts->flags & ~(ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP)) != 0) return ALIBI_EINVAL;
+    if ((opts->flags & ALIBI_CLAMP) && !std::isfinite(opts->clamp_min)) return ALIBI_EINVAL;
+    if ((opts->flags & ALIBI_SOFTCAP) && !(std::isfinite(opts->softcap) && opts->softcap > 0.0f))
+      return ALIBI_EINVAL;
+    if (opts->q_offset < 0 || opts->q_offset > kMaxLen || opts->k_offset < 0 || opts->k_offset > kMaxLen)
+      return ALIBI_EINVAL;
+    opt->flags = opts->flags;
+    opt->clamp_min = opts->clamp_min;
+    opt->softcap = opts->softcap;
+    opt->q_offset = opts->q_offset;
+    opt->k_offset = opts->k_offset;
+  }
+  if ((long long)B * H * Nk > (1LL << 31) * 4) return ALIBI_ENOTSUP;
+  return ALIBI_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? ALIBI_OK : ALIBI_EHIP; }
 
 // ---- decode workspace: one growable buffer per device ----
@@ -94,27 +120,64 @@ int alibi_slopes(int H, float* slopes_out) {
 
 int alibi_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
                    int d, const float* slopes, int causal, hipStream_t stream) {
-  int st = check_common(q, k, v, out, slopes, B, H, N, d, 16);
-  if (st != ALIBI_OK) return st;
-  if (causal != 0 && causal != 1) return ALIBI_EINVAL;
-  if (d > 256 || d % 8 != 0) return ALIBI_ENOTSUP;
-  const float c1 = scale_log2(d);
-  if (d == 64 || d == 128) {
-    if (log_enabled()) std::fprintf(stderr, "[alibi] fwd mfma B=%d H=%d N=%d d=%d causal=%d\n", B, H, N, d, causal);
-    return hip_status(alibi::launch_fwd_mfma(q, k, v, out, B, H, N, d, slopes, causal, c1, stream));
-  }
-  if (log_enabled()) std::fprintf(stderr, "[alibi] fwd generic bf16 B=%d H=%d N=%d d=%d\n", B, H, N, d);
-  return hip_status(alibi::launch_fwd_generic_bf16(q, k, v, out, B, H, N, d, slopes, causal, c1, stream));
+  return alibi_attn_fwd_ex(q, k, v, out, B, H, N, N, d, slopes, causal, nullptr, stream);
 }
 
 int alibi_attn_fwd_f32(const float* q, const float* k, const float* v, float* out, int B, int H,
                        int N, int d, const float* slopes, int causal, hipStream_t stream) {
-  int st = check_common(q, k, v, out, slopes, B, H, N, d, 4);
+  return alibi_attn_fwd_ex_f32(q, k, v, out, B, H, N, N, d, slopes, causal, nullptr, stream);
+}
+
+int alibi_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
+                      int Nk, int d, const float* slopes, int causal, const alibi_fwd_opts* opts,
+                      hipStream_t stream) {
+  alibi::FwdOptions opt;
+  int st = check_fwd(q, k, v, out, slopes, B, H, Nq, Nk, d, causal, opts, 16, &opt);
   if (st != ALIBI_OK) return st;
-  if (causal != 0 && causal != 1) return ALIBI_EINVAL;
+  if (d > 256 || d % 8 != 0) return ALIBI_ENOTSUP;
+  const alibi::FwdArgs a{q, k, v, out, B, H, Nq, Nk, d, slopes, causal};
+  if (d == 64 || d == 128) {
+    if (log_enabled())
+      std::fprintf(stderr, "[alibi] fwd mfma B=%d H=%d Nq=%d Nk=%d d=%d causal=%d flags=%d offsets=%d,%d\n",
+                   B, H, Nq, Nk, d, causal, opt.flags, opt.q_offset, opt.k_offset);
+    return hip_status(alibi::launch_fwd_mfma(a, opt, scale_log2(d), stream));
+  }
+  if (log_enabled()) std::fprintf(stderr, "[alibi] fwd generic bf16 B=%d H=%d Nq=%d Nk=%d d=%d\n", B, H, Nq, Nk, d);
+  return hip_status(alibi::launch_fwd_generic(a, opt, false, stream));
+}
+
+int alibi_attn_fwd_ex_f32(const float* q, const float* k, const float* v, float* out, int B, int H,
+                          int Nq, int Nk, int d, const float* slopes, int causal,
+                          const alibi_fwd_opts* opts, hipStream_t stream) {
+  alibi::FwdOptions opt;
+  int st = check_fwd(q, k, v, out, slopes, B, H, Nq, Nk, d, causal, opts, 4, &opt);
+  if (st != ALIBI_OK) return st;
   if (d > 256) return ALIBI_ENOTSUP;
-  return hip_status(alibi::launch_fwd_generic_f32(q, k, v, out, B, H, N, d, slopes, causal,
-                                                  scale_log2(d), stream));
+  const alibi::FwdArgs a{q, k, v, out, B, H, Nq, Nk, d, slopes, causal};
+  return hip_status(alibi::launch_fwd_generic(a, opt, true, stream));
+}
+
+int alibi_slopes_recipe(int recipe, int H, int log_distance, float* slopes_out) {
+  if (H < 1 || slopes_out == nullptr) return ALIBI_EINVAL;
+  if (recipe == ALIBI_SLOPES_DEFAULT) return alibi_slopes(H, slopes_out);
+  double lo = 0.0, hi = 0.0;
+  switch (recipe) {
+    case ALIBI_SLOPES_STEEP: lo = 128.0; hi = 512.0; break;
+    case ALIBI_SLOPES_SAFE: lo = 2048.0; hi = 4096.0; break;
+    case ALIBI_SLOPES_WIDE: lo = 16.0; hi = 4096.0; break;
+    case ALIBI_SLOPES_EXPLICIT: break;
+    default: return ALIBI_EINVAL;
+  }
+  const double tau = 126.0 * std::log(2.0);  // |ln 2^-126|
+  for (int h = 0; h < H; ++h) {
+    double delta;
+    if (recipe == ALIBI_SLOPES_EXPLICIT)
+      delta = 32.0 * std::exp2(double(h));
+    else
+      delta = H == 1 ? lo : lo * std::pow(hi / lo, double(h) / double(H - 1));
+    slopes_out[h] = float(log_distance ? tau / std::log(delta + 1.0) : tau / delta);
+  }
+  return ALIBI_OK;
 }
 
 int alibi_attn_decode(const void* q, const void* kcache, const void* vcache, void* out, int B,

@@ -7,6 +7,9 @@
 //   t_j = (q_i . k_j) / sqrt(d) - m_h * dist(i, j),   dist = i - j (causal, j <= i)
 //                                                      or |i - j| (not causal)
 //   out_i = sum_j softmax(t)_j v_j
+// with positions shifted by the query/key offsets, and optionally the Sec. 3.4
+// mitigations of the same paper (bias floor, ln(D + 1) distances, soft-capped
+// content logits), evaluated with the precise device math library.
 // with an fp32 online softmax in log2 units. One wave owns one query row: the
 // head dimension is spread over the 64 lanes (up to 4 values per lane), the
 // dot product is a wave reduction, and the keys are walked in order.
@@ -14,6 +17,8 @@
 // hot path is the MFMA kernel.
 #include "device_common.h"
 #include "launch.h"
+
+#include <cmath>
 
 namespace alibi {
 
@@ -24,20 +29,31 @@ template <typename T> __device__ __forceinline__ void store_f(T* p, float x);
 template <> __device__ __forceinline__ void store_f<float>(float* p, float x) { *p = x; }
 template <> __device__ __forceinline__ void store_f<uint16_t>(uint16_t* p, float x) { *p = f32_to_bf16(x); }
 
+// Run-time description of one generic launch (natural-log units).
+struct GenParams {
+  int flags;        // bits 1 clamp, 2 log distance, 4 soft cap (Sec. 3.4 mitigations)
+  float clamp_min;  // bias floor
+  float softcap;    // z of z tanh(A / z)
+  int delta;        // position of query row 0 minus position of key row 0
+  float inv_sqrt_d;
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void fwd_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
-    int H, int N, int d, long long rows, const float* __restrict__ slopes, int causal, float c1) {
+    int H, int Nq, int Nk, int d, long long rows, const float* __restrict__ slopes, int causal,
+    GenParams gp) {
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const long long bh = row / N;
-  const int i = int(row - bh * N);
+  const long long bh = row / Nq;
+  const int i = int(row - bh * Nq);
+  const int pi = i + gp.delta;  // key-index position of this query
   const int h = int(bh % H);
-  const float c2 = slopes[h] * kLog2e;
+  const float m = slopes[h];
   const T* qr = q + row * d;
-  const T* kb = k + bh * (long long)N * d;
-  const T* vb = v + bh * (long long)N * d;
+  const T* kb = k + bh * (long long)Nk * d;
+  const T* vb = v + bh * (long long)Nk * d;
 
   float qv[4], acc[4];
 #pragma unroll
@@ -47,7 +63,7 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(
     acc[e] = 0.0f;
   }
   float m_run = kNegInf, l_run = 0.0f;
-  const int jend = causal ? i + 1 : N;
+  const int jend = causal ? max(0, min(Nk, pi + 1)) : Nk;
   for (int j = 0; j < jend; ++j) {
     float part = 0.0f;
 #pragma unroll
@@ -55,9 +71,17 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(
       const int dd = lane + 64 * e;
       if (dd < d) part += qv[e] * load_f(kb + (long long)j * d + dd);
     }
-    const float s = wave_sum(part);
-    const int dist = i - j;
-    const float t = s * c1 - c2 * float(dist < 0 ? -dist : dist);
+    // A = q.k / sqrt(d), soft-capped to z tanh(A / z); D = |pi - j| (= pi - j
+    // under the causal mask), log-scaled to ln(D + 1); B = -m D, floored at
+    // the clamp; the exponent is (A + B) in log2 units
+    float a = wave_sum(part) * gp.inv_sqrt_d;
+    if (gp.flags & 4) a = gp.softcap * tanhf(a / gp.softcap);
+    const int dist = pi - j;
+    float dd = float(dist < 0 ? -dist : dist);
+    if (gp.flags & 2) dd = log1pf(dd);
+    float bias = -m * dd;
+    if (gp.flags & 1) bias = fmaxf(bias, gp.clamp_min);
+    const float t = (a + bias) * kLog2e;
     const float m_new = fmaxf(m_run, t);
     const float alpha = fast_exp2(m_run - m_new);  // exp2(-inf) = 0 on the first key
     const float p = fast_exp2(t - m_new);
@@ -70,7 +94,7 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(
     }
     m_run = m_new;
   }
-  const float inv = 1.0f / l_run;
+  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;  // a row that saw no key gives 0
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int dd = lane + 64 * e;
@@ -121,24 +145,23 @@ __global__ __launch_bounds__(256) void weights_f32_kernel(
   }
 }
 
-hipError_t launch_fwd_generic_f32(const float* q, const float* k, const float* v, float* out,
-                                  int B, int H, int N, int d, const float* slopes, int causal,
-                                  float c1, hipStream_t stream) {
-  const long long rows = (long long)B * H * N;
+hipError_t launch_fwd_generic(const FwdArgs& a, const FwdOptions& opt, bool f32, hipStream_t stream) {
+  const long long rows = (long long)a.B * a.H * a.Nq;
   const unsigned grid = unsigned((rows + 3) / 4);
-  hipLaunchKernelGGL(fwd_generic_kernel<float>, dim3(grid), dim3(256), 0, stream,
-                     q, k, v, out, H, N, d, rows, slopes, causal, c1);
-  return hipGetLastError();
-}
-
-hipError_t launch_fwd_generic_bf16(const void* q, const void* k, const void* v, void* out,
-                                   int B, int H, int N, int d, const float* slopes, int causal,
-                                   float c1, hipStream_t stream) {
-  const long long rows = (long long)B * H * N;
-  const unsigned grid = unsigned((rows + 3) / 4);
-  hipLaunchKernelGGL(fwd_generic_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out,
-                     H, N, d, rows, slopes, causal, c1);
+  GenParams gp;
+  gp.flags = opt.flags;
+  gp.clamp_min = opt.clamp_min;
+  gp.softcap = opt.softcap;
+  gp.delta = opt.q_offset - opt.k_offset;
+  gp.inv_sqrt_d = float(1.0 / std::sqrt(double(a.d)));
+  if (f32)
+    hipLaunchKernelGGL(fwd_generic_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,
+                       a.H, a.Nq, a.Nk, a.d, rows, a.slopes, a.causal, gp);
+  else
+    hipLaunchKernelGGL(fwd_generic_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (uint16_t*)a.out, a.H, a.Nq, a.Nk, a.d, rows, a.slopes, a.causal, gp);
   return hipGetLastError();
 }
 

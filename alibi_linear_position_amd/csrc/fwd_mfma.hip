@@ -68,6 +68,9 @@ int fwd_waves() {
   return nw;
 }
 constexpr float kLazy = 8.0f;
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family parts:
+// 32-bit data format, byte-granular range check against the record count.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -115,33 +118,25 @@ struct TileRegs {
   u32x4 k[LOADS];
   u32x4 v[LOADS];
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
-                                       long long base, int j0, int N, int tid) {
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int c = tid + NT * r;
-      const int row = c / CPR, col = c % CPR;
-      k[r] = u32x4{0u, 0u, 0u, 0u};
-      if (j0 + row < N) k[r] = *reinterpret_cast<const u32x4*>(kg + base + (long long)(j0 + row) * D + col * 8);
-      const int key = tid % BN;
-      const int vcol = tid / BN + (NT / BN) * r;
-      v[r] = u32x4{0u, 0u, 0u, 0u};
-      if (j0 + key < N) v[r] = *reinterpret_cast<const u32x4*>(vg + base + (long long)(j0 + key) * D + vcol * 8);
-    }
+  // Loads of one tile through buffer resources: chunk r of K sits at byte
+  // 16 (tid + NT r) of the tile (rows are contiguous), chunk r of V at byte
+  // 2 (key D + 8 (tid / BN + (NT / BN) r)). Each thread's byte offset is fixed
+  // and the tile's byte offset `tb` is a scalar, so a load carries no per-tile
+  // vector address arithmetic. A resource whose range ends at row Nk makes
+  // rows past it read as zero when the tile starts at the resource's base
+  // (tb = 0: the range check covers the vector offset).
+  static __device__ __forceinline__ uint32_t k_off(int tid) { return uint32_t(tid) * 16u; }
+  static __device__ __forceinline__ uint32_t v_off(int tid) {
+    return (uint32_t(tid % BN) * D + uint32_t(tid / BN) * 8u) * 2u;
   }
-
-  // A tile that lies entirely below N: no guards and no zero fill. Chunk r of
-  // K sits at element (tid + NT r) * 8 of the tile (rows are contiguous), chunk
-  // r of V at key * D + (tid / BN + (NT / BN) r) * 8: one per-thread offset
-  // plus a constant per chunk.
-  __device__ __forceinline__ void load_full(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
-                                            int tid) {
-    const uint32_t koff = uint32_t(tid) * 8u;
-    const uint32_t voff = uint32_t(tid % BN) * D + uint32_t(tid / BN) * 8u;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t tb,
+                                       uint32_t koff, uint32_t voff) {
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
-      k[r] = *reinterpret_cast<const u32x4*>(kt + koff + uint32_t(NT * 8 * r));
-      v[r] = *reinterpret_cast<const u32x4*>(vt + voff + uint32_t((NT / BN) * 8 * r));
+      k[r] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, int(tb + uint32_t(NT * 16 * r)), 0));
+      v[r] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, int(tb + uint32_t((NT / BN) * 16 * r)), 0));
     }
   }
 
@@ -165,11 +160,24 @@ struct TileRegs {
   }
 };
 
-template <int D, int NW, bool CAUSAL>
+// Mitigation variants (Sec. 3.4 of "When Attention Goes Blind"), as bits of the
+// kernel's VAR template argument: the bias floored at a constant, the distance
+// replaced by ln(D + 1), the content logit soft-capped as z tanh(A / z).
+constexpr int kVarClamp = 1, kVarLog = 2, kVarSoftcap = 4;
+
+// Run-time parameters of a variant launch, all in log2 units of the scores.
+struct FwdVariant {
+  int delta;      // position of query row 0 minus position of key row 0
+  float clamp2;   // bias floor c_clamp log2(e)
+  float cap_in;   // 2 log2(e) / (sqrt(d) z): exp2(s cap_in) = e^(2 A / z) for s = q.k
+  float cap_out;  // z log2(e)
+};
+
+template <int D, int NW, bool CAUSAL, int VAR>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, int H, int N, int nqb, int total, const float* __restrict__ slopes,
-    float c1) {
+    uint16_t* __restrict__ out, int H, int Nq, int Nk, int nqb, int total,
+    const float* __restrict__ slopes, float c1, FwdVariant var) {
   constexpr int NT = NW * 64;
   constexpr int BN = 64;
   constexpr int BM = NW * 32;
@@ -197,27 +205,34 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   const int bh = lw / nqb;
   const int qblk = nqb - 1 - (lw - bh * nqb);
   const int h = bh % H;
-  const float c2 = slopes[h] * kLog2e;
-  const long long base = (long long)bh * N * D;
+  const float mh = slopes[h];
+  const float c2 = mh * kLog2e;
+  const long long qbase = (long long)bh * Nq * D;
+  const long long kbase = (long long)bh * Nk * D;
   const int q0 = qblk * BM;
-  const int qw0 = q0 + wave * 32;                      // first query of this wave
-  const int qw_last = min(qw0 + 32, N) - 1;            // last valid query of this wave
-  const int i = qw0 + l32;                             // this lane's query
+  const int qw0 = q0 + wave * 32;                      // first query row of this wave
+  const int qw_last = min(qw0 + 32, Nq) - 1;           // last valid query row of this wave
+  const int i = qw0 + l32;                             // this lane's query row
+  // Query row i sits at key-index position pi: key j is visible to it when
+  // j <= pi (causal) and lies at distance pi - j.
+  const int delta = var.delta;
+  const int pi = i + delta;
 
   // C operand of the first Q K^T k-step: seeds register r of a 32-key block
-  // with its bias offset m log2(e) (8 (r / 4) + r % 4) / c1, so off-diagonal
-  // tiles need one fma per score to complete the bias.
+  // with its bias offset m log2(e) (8 (r / 4) + r % 4) / c1, so tiles without
+  // a mask need one fma per score to complete the linear bias. Variants keep
+  // the plain content score (their bias is not linear in the key index).
   f32x16 cinit;
   const float c21 = c2 / c1;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) cinit[r] = c21 * float(8 * (r >> 2) + (r & 3));
+  for (int r = 0; r < 16; ++r) cinit[r] = VAR == 0 ? c21 * float(8 * (r >> 2) + (r & 3)) : 0.0f;
 
   // Q^T fragments (MFMA B operand): lane holds query l32, d = 16 ks + 8 hi .. +7.
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (i < N) raw = *reinterpret_cast<const u32x4*>(q + base + (long long)i * D + 16 * ks + 8 * hi);
+    if (i < Nq) raw = *reinterpret_cast<const u32x4*>(q + qbase + (long long)i * D + 16 * ks + 8 * hi);
     qf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
 
@@ -226,29 +241,68 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.0f;
 
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  // Keys any query of the block can see: [0, kend).
+  const int kend = CAUSAL ? max(0, min(Nk, q0 + BM - 1 + delta + 1)) : Nk;
   const int ntiles = (kend + BN - 1) / BN;
 
   TileRegs<D, NT> regs;
-  regs.load(k, v, base, (ntiles - 1) * BN, N, tid);
-  regs.template store<KPITCH, VPITCH>(smem, smem + KBYTES, tid);
+  const uint32_t koff = TileRegs<D, NT>::k_off(tid), voff = TileRegs<D, NT>::v_off(tid);
+  // K and V rows of this (b, h): Nk D bf16 each, at most 2^24 rows of 128
+  // values (2^32 bytes); the range is capped at 2^32 - 1 bytes, which no valid
+  // 16-byte chunk reaches. Byte offsets are 32-bit unsigned.
+  auto rsrc = [&](const uint16_t* p, long long rows) {
+    const uint32_t bytes = uint32_t(min(rows * D * 2, 0xffffffffLL));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, int(bytes), kBufferFlags);
+  };
+  const __amdgpu_buffer_rsrc_t rk = rsrc(k + kbase, Nk), rv = rsrc(v + kbase, Nk);
+  {
+    // The first tile visited is the only one that can reach past Nk: stage it
+    // through resources that start at the tile, so missing rows read as zero.
+    // With no tile to visit (every query before every key) tile 0 is staged
+    // and never read.
+    const int jp = max(ntiles - 1, 0) * BN;
+    regs.load(rsrc(k + kbase + (long long)jp * D, Nk - jp), rsrc(v + kbase + (long long)jp * D, Nk - jp), 0u,
+              koff, voff);
+    regs.template store<KPITCH, VPITCH>(smem, smem + KBYTES, tid);
+  }
+
+  // Exponent of one score (log2 units) for the variants, from the plain
+  // content score s = q.k and the signed distance pi - j (an exact integer).
+  auto variant_t = [&](float s, float dist) {
+    float a;
+    if constexpr ((VAR & kVarSoftcap) != 0) {
+      // z tanh(A / z) = z (1 - 2 / (e^(2 A / z) + 1)); saturates to +-z
+      const float e2 = fast_exp2(s * var.cap_in);
+      a = var.cap_out * fmaf(-2.0f, __builtin_amdgcn_rcpf(e2 + 1.0f), 1.0f);
+    } else {
+      a = s * c1;
+    }
+    const float dd = CAUSAL ? dist : fabsf(dist);
+    float b;
+    if constexpr ((VAR & kVarLog) != 0) {
+      b = -mh * __builtin_amdgcn_logf(dd + 1.0f);  // -m ln(D + 1) log2(e) = -m log2(D + 1)
+    } else {
+      b = -c2 * dd;
+    }
+    if constexpr ((VAR & kVarClamp) != 0) b = fmaxf(b, var.clamp2);
+    return a + b;
+  };
 
   // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T, and the LDS stores
   // of the next tile (whose global loads were issued at the top). MASKED tiles
-  // may hold keys past a query or past N; the others hold none for any wave.
+  // may hold keys past a query or past Nk; the others hold none for any wave.
   int stage = 0;
   auto step = [&](int tile, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int j0 = tile * BN;
     // Stage `stage` holds this tile; every wave is done with the other stage.
     __syncthreads();
-    // Only the first tile visited can be ragged, and the prologue staged it.
-    if (tile > 0) regs.load_full(k + base + (long long)(j0 - BN) * D, v + base + (long long)(j0 - BN) * D, tid);
+    if (tile > 0) regs.load(rk, rv, uint32_t(j0 - BN) * (D * 2), koff, voff);  // in flight during this tile
     const unsigned char* sK = smem + stage * STAGE;
     const unsigned char* sV = sK + KBYTES;
     unsigned char* const sKn = smem + (stage ^ 1) * STAGE;
     stage ^= 1;
-    if (MASKED && !(qw0 < N && (!CAUSAL || j0 <= qw_last))) {
+    if (MASKED && !(qw0 < Nq && (!CAUSAL || j0 <= qw_last + delta))) {
       regs.template store<KPITCH, VPITCH>(sKn, sKn + KBYTES, tid);
       return;
     }
@@ -265,12 +319,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     }
 
     // ---- bias, mask, online softmax ----
-    // s = q.k + (c2 / c1)(8 (r / 4) + r % 4); the full exponent is
-    // t = s c1 + c2 (j0 + 32 kb + 4 hi - i).
-    const float bt0 = c2 * float(j0 + 4 * hi - i);
+    // Plain ALiBi: s = q.k + (c2 / c1)(8 (r / 4) + r % 4) and the exponent is
+    // t = s c1 + c2 (j0 + 32 kb + 4 hi - pi). Variants: s becomes t itself.
+    const float bt0 = c2 * float(j0 + 4 * hi - pi);
     const float bt1 = bt0 + 32.0f * c2;
+    const float dpos = float(pi - j0 - 4 * hi);  // distance of register 0 of key block 0
     float mcand;
-    if (!MASKED) {
+    if (VAR == 0 && !MASKED) {
       // every key is visible: max16 of s bounds the row maximum
       mcand = max_xor32(fmaxf(fmaf(max16(s[0]), c1, bt0), fmaf(max16(s[1]), c1, bt1)));
     } else {
@@ -280,12 +335,18 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool valid = j < N && (!CAUSAL || j <= i);
-          float x = s[kb][r];
-          if (!CAUSAL && j > i) x -= 2.0f * c21 * float(j - i);  // symmetric bias -m |i - j|
-          s[kb][r] = valid ? x : kNegInf;
-          tmax = fmaxf(tmax, fmaf(s[kb][r], c1, kb ? bt1 : bt0));
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const int j = j0 + 4 * hi + off;
+          float x;
+          if constexpr (VAR == 0) {
+            x = s[kb][r];
+            if (!CAUSAL && j > pi) x -= 2.0f * c21 * float(j - pi);  // symmetric bias -m |i - j|
+          } else {
+            x = variant_t(s[kb][r], dpos - float(off));
+          }
+          if (MASKED) x = (j < Nk && (!CAUSAL || j <= pi)) ? x : kNegInf;
+          s[kb][r] = x;
+          tmax = fmaxf(tmax, VAR == 0 ? fmaf(x, c1, kb ? bt1 : bt0) : x);
         }
       }
       mcand = max_xor32(tmax);
@@ -306,7 +367,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const float m_use = MASKED && m_run == kNegInf ? 0.0f : m_run;
     u32x4 pf[PS];
     float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
-    const float b0 = bt0 - m_use, b1 = bt1 - m_use;
+    const float sc = VAR == 0 ? c1 : 1.0f;
+    const float b0 = (VAR == 0 ? bt0 : 0.0f) - m_use, b1 = (VAR == 0 ? bt1 : 0.0f) - m_use;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -316,7 +378,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r0 = 8 * half + 2 * e;
           const float bb = kb ? b1 : b0;
-          pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], c1, bb)), fast_exp2(fmaf(s[kb][r0 + 1], c1, bb)));
+          pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], sc, bb)), fast_exp2(fmaf(s[kb][r0 + 1], sc, bb)));
           lpart[e] = bdot2(pk[e], lpart[e]);
         }
         pf[2 * kb + half] = pk;
@@ -338,18 +400,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     regs.template store<KPITCH, VPITCH>(sKn, sKn + KBYTES, tid);
   };
 
-  // Tiles 0 .. t_open lie wholly below the workgroup's first query q0 (so below
-  // every wave's queries, and below N): no mask. The rest, at most
-  // (BM + BN - 1) / BN of them under the causal mask, take the masked path.
-  const int t_open = CAUSAL ? (q0 + 1) / BN - 1 : -1;
+  // Tiles 0 .. t_open hold only keys at or before the block's first query
+  // position q0 + delta (so before every wave's queries) and lie wholly below
+  // Nk: no mask. The rest, at most (BM + BN - 1) / BN + 1 of them under the
+  // causal mask, take the masked path; without the mask every tile does.
+  int t_open = -1;
+  if (CAUSAL) {
+    const int x = q0 + delta + 1;                      // keys [0, x) are visible to every query
+    t_open = x < BN ? -1 : min(min(x / BN - 1, Nk / BN - 1), ntiles - 1);
+  }
   int tile = ntiles - 1;
   for (; tile > t_open; --tile) step(tile, std::true_type{});
   for (; tile >= 0; --tile) step(tile, std::false_type{});
 
-  // ---- epilogue: O / l -> bf16 ----
+  // ---- epilogue: O / l -> bf16; a row that saw no key gives 0 ----
   const float lt = sum_xor32(l_run);
-  const float inv = 1.0f / lt;
-  if (i < N) {
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (i < Nq) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -357,41 +424,53 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
         u32x2 st;
         st[0] = pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
         st[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(out + base + (long long)i * D + 32 * db + 8 * g + 4 * hi) = st;
+        *reinterpret_cast<u32x2*>(out + qbase + (long long)i * D + 32 * db + 8 * g + 4 * hi) = st;
       }
     }
   }
 }
 
-template <int D, int NW, bool CAUSAL>
-hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
-                      const float* slopes, float c1, hipStream_t stream) {
+template <int D, int NW, bool CAUSAL, int VAR>
+hipError_t launch_cfg(const FwdArgs& a, float c1, const FwdVariant& var, hipStream_t stream) {
   constexpr int BM = NW * 32;
-  const int nqb = (N + BM - 1) / BM;
-  const long long total = (long long)B * H * nqb;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, CAUSAL>), dim3(unsigned(total)), dim3(NW * 64), 0,
-                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                     (uint16_t*)out, H, N, nqb, int(total), slopes, c1);
+  const int nqb = (a.Nq + BM - 1) / BM;
+  const long long total = (long long)a.B * a.H * nqb;
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, CAUSAL, VAR>), dim3(unsigned(total)), dim3(NW * 64), 0,
+                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.out, a.H, a.Nq, a.Nk, nqb, int(total), a.slopes, c1, var);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_var(const FwdArgs& a, int flags, float c1, const FwdVariant& var, hipStream_t s) {
+  switch (flags) {
+    case 0: return fwd_waves() == 8 ? launch_cfg<D, 8, CAUSAL, 0>(a, c1, var, s)
+                                    : launch_cfg<D, 4, CAUSAL, 0>(a, c1, var, s);
+    case 1: return launch_cfg<D, 4, CAUSAL, 1>(a, c1, var, s);
+    case 2: return launch_cfg<D, 4, CAUSAL, 2>(a, c1, var, s);
+    case 3: return launch_cfg<D, 4, CAUSAL, 3>(a, c1, var, s);
+    case 4: return launch_cfg<D, 4, CAUSAL, 4>(a, c1, var, s);
+    case 5: return launch_cfg<D, 4, CAUSAL, 5>(a, c1, var, s);
+    case 6: return launch_cfg<D, 4, CAUSAL, 6>(a, c1, var, s);
+    default: return launch_cfg<D, 4, CAUSAL, 7>(a, c1, var, s);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, void* out,
-                           int B, int H, int N, int d, const float* slopes, int causal,
-                           float c1, hipStream_t stream) {
-  if (fwd_waves() == 4) {
-    if (d == 128)
-      return causal ? launch_cfg<128, 4, true>(q, k, v, out, B, H, N, slopes, c1, stream)
-                    : launch_cfg<128, 4, false>(q, k, v, out, B, H, N, slopes, c1, stream);
-    return causal ? launch_cfg<64, 4, true>(q, k, v, out, B, H, N, slopes, c1, stream)
-                  : launch_cfg<64, 4, false>(q, k, v, out, B, H, N, slopes, c1, stream);
-  }
-  if (d == 128)
-    return causal ? launch_cfg<128, 8, true>(q, k, v, out, B, H, N, slopes, c1, stream)
-                  : launch_cfg<128, 8, false>(q, k, v, out, B, H, N, slopes, c1, stream);
-  return causal ? launch_cfg<64, 8, true>(q, k, v, out, B, H, N, slopes, c1, stream)
-                : launch_cfg<64, 8, false>(q, k, v, out, B, H, N, slopes, c1, stream);
+hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hipStream_t stream) {
+  FwdVariant var;
+  var.delta = opt.q_offset - opt.k_offset;
+  var.clamp2 = opt.clamp_min * kLog2e;
+  const double z = opt.softcap > 0.0f ? double(opt.softcap) : 1.0;
+  var.cap_in = float(2.0 * double(c1) / z);
+  var.cap_out = float(z * 1.4426950408889634);
+  const int flags = opt.flags & 7;
+  if (a.d == 128)
+    return a.causal ? launch_var<128, true>(a, flags, c1, var, stream)
+                    : launch_var<128, false>(a, flags, c1, var, stream);
+  return a.causal ? launch_var<64, true>(a, flags, c1, var, stream)
+                  : launch_var<64, false>(a, flags, c1, var, stream);
 }
 
 }  // namespace alibi

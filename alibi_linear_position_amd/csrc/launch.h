@@ -7,19 +7,36 @@
 
 namespace alibi {
 
-hipError_t launch_fwd_generic_f32(const float* q, const float* k, const float* v, float* out,
-                                  int B, int H, int N, int d, const float* slopes, int causal,
-                                  float c1, hipStream_t stream);
-hipError_t launch_fwd_generic_bf16(const void* q, const void* k, const void* v, void* out,
-                                   int B, int H, int N, int d, const float* slopes, int causal,
-                                   float c1, hipStream_t stream);
 hipError_t launch_weights_f32(const float* q, const float* k, float* w, int B, int H, int N, int d,
                               const float* slopes, int causal, float c1, hipStream_t stream);
 
+// One forward call: q/out (B, H, Nq, d), k/v (B, H, Nk, d), device pointers.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int B, H, Nq, Nk, d;
+  const float* slopes;
+  int causal;
+};
+
+// Mitigations and positions (validated by the caller): flags are the
+// ALIBI_CLAMP / ALIBI_LOG_DISTANCE / ALIBI_SOFTCAP bits; query row r sits at
+// position q_offset + r and key row c at k_offset + c.
+struct FwdOptions {
+  int flags = 0;
+  float clamp_min = 0.0f;
+  float softcap = 0.0f;
+  int q_offset = 0;
+  int k_offset = 0;
+};
+
+// Generic (VALU) forward, any d <= 256: fp32 (f32 = true) or bf16 data.
+hipError_t launch_fwd_generic(const FwdArgs& a, const FwdOptions& opt, bool f32, hipStream_t stream);
+
 // MFMA forward, bf16, d in {64, 128}.
-hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, void* out,
-                           int B, int H, int N, int d, const float* slopes, int causal,
-                           float c1, hipStream_t stream);
+hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hipStream_t stream);
 
 // Split-KV decode. `splits` key ranges of `chunk` keys each; ws holds
 // B*H*splits*(d+2) floats when splits > 1 (may be null when splits == 1).

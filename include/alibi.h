@@ -117,6 +117,82 @@ int alibi_attn_weights_f32(const float* q, const float* k, float* w,
                            int B, int H, int N, int d, const float* slopes, int causal,
                            hipStream_t stream);
 
+/*
+ * Extended forward: mitigation variants and query/key position offsets.
+ *
+ * Mitigations (Sec. 3.4 of "When Attention Goes Blind", settings of Sec. 4.3):
+ *   ALIBI_CLAMP         bias floored at a constant: B* = max(B, clamp_min)
+ *   ALIBI_LOG_DISTANCE  distance compressed: D* = ln(D + 1), so B = -m ln(D + 1)
+ *   ALIBI_SOFTCAP       content logit capped: A* = softcap * tanh(A / softcap),
+ *                       A = q.k / sqrt(d); the bias is not capped
+ * Any combination is allowed; per score the order is A -> A*, D -> D*,
+ * B = -m D*, B -> B*, logit = A* + B*, then the causal mask and the softmax.
+ */
+#define ALIBI_CLAMP 1
+#define ALIBI_LOG_DISTANCE 2
+#define ALIBI_SOFTCAP 4
+
+typedef struct alibi_fwd_opts {
+  int flags;         /* OR of the ALIBI_* mitigation bits; other bits -> ALIBI_EINVAL */
+  float clamp_min;   /* bias floor in logit units (e.g. -87); finite; used with ALIBI_CLAMP */
+  float softcap;     /* z > 0, finite (e.g. 50); used with ALIBI_SOFTCAP */
+  int q_offset;      /* position of query row 0, 0 .. 2^24 */
+  int k_offset;      /* position of key row 0, 0 .. 2^24 */
+} alibi_fwd_opts;
+
+/*
+ * q, out: device bf16 (B, H, Nq, d); k, v: device bf16 (B, H, Nk, d).
+ * Query row r sits at position q_offset + r and key row c at k_offset + c; the
+ * distance is the difference of the positions (abhik.ai, KV-cache remark: a
+ * cached query keeps its real position). With causal = 1 key c is visible to
+ * query r when its position is not later; a query that sees no key gets a zero
+ * output row. A chunk of Nq new tokens after Nk - Nq cached ones is
+ * q_offset = Nk - Nq, k_offset = 0 (chunked prefill).
+ * opts may be NULL (no mitigation, both offsets 0); alibi_attn_fwd is this call
+ * with Nq = Nk = N and opts = NULL. d in {64, 128} runs the MFMA kernel (each
+ * mitigation mix is its own compiled variant); other d (multiples of 8 up to
+ * 256) the generic kernel. Errors: as alibi_attn_fwd, plus ALIBI_EINVAL for an
+ * unknown flag bit, a non-finite clamp, a soft cap that is not positive and
+ * finite, or an offset outside 0 .. 2^24.
+ */
+int alibi_attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
+                      int B, int H, int Nq, int Nk, int d, const float* slopes, int causal,
+                      const alibi_fwd_opts* opts, hipStream_t stream);
+
+/*
+ * Same operation in fp32 through the generic kernel, with the mitigations
+ * evaluated by the precise device math library (tanhf, log1pf); for exact
+ * checks. Any 1 <= d <= 256, 4-byte aligned pointers.
+ */
+int alibi_attn_fwd_ex_f32(const float* q, const float* k, const float* v, float* out,
+                          int B, int H, int Nq, int Nk, int d, const float* slopes, int causal,
+                          const alibi_fwd_opts* opts, hipStream_t stream);
+
+/*
+ * Slope recipes from target blindness distances (host only). A head whose bias
+ * should reach the fp32 underflow limit ln 2^-126 at distance delta gets
+ * m = 126 ln(2) / delta ("When Attention Goes Blind": Sec. 3.2 blindness
+ * distance, Sec. 3.4 "Robust Slopes", Sec. 4.2 configurations, App. F Table 8;
+ * the printed distances follow that threshold). Targets, steepest head first,
+ * spaced geometrically from the first to the last:
+ *   ALIBI_SLOPES_STEEP     128 .. 512
+ *   ALIBI_SLOPES_SAFE      2048 .. 4096
+ *   ALIBI_SLOPES_WIDE      16 .. 4096
+ *   ALIBI_SLOPES_EXPLICIT  32, 64, 128, ... (doubling, as Table 8 lists them)
+ *   ALIBI_SLOPES_DEFAULT   the geometric schedule of alibi_slopes
+ * log_distance != 0 adapts a target recipe to ALIBI_LOG_DISTANCE:
+ * m = 126 ln(2) / ln(delta + 1) (Sec. 4.3); it does not change the default.
+ * Each slope is evaluated in double and rounded to nearest-even fp32.
+ * slopes_out: HOST array of H floats. Errors: H < 1, an unknown recipe or a
+ * NULL pointer -> ALIBI_EINVAL.
+ */
+#define ALIBI_SLOPES_DEFAULT 0
+#define ALIBI_SLOPES_STEEP 1
+#define ALIBI_SLOPES_SAFE 2
+#define ALIBI_SLOPES_WIDE 3
+#define ALIBI_SLOPES_EXPLICIT 4
+int alibi_slopes_recipe(int recipe, int H, int log_distance, float* slopes_out);
+
 /* Static, never-NULL description of a status code. */
 const char* alibi_status_string(int status);
 

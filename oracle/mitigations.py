@@ -71,7 +71,7 @@ def slopes_recipe_ref(recipe: str, H: int, log_distance: bool = False) -> np.nda
     """
     dl = recipe_distances(recipe, H)
     if log_distance:
-        m = TAU_D / np.log(dl + 1.0)
+        m = TAU_D / np.array([math.log(x + 1.0) for x in dl])
     else:
         m = TAU_D / dl
     return m.astype(np.float32)

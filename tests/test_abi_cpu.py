@@ -31,7 +31,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("alibi_slopes", "alibi_attn_fwd", "alibi_attn_decode", "alibi_attn_fwd_f32",
-              "alibi_attn_weights_f32", "alibi_status_string", "alibi_release"):
+              "alibi_attn_weights_f32", "alibi_status_string", "alibi_release",
+              "alibi_attn_fwd_ex", "alibi_attn_fwd_ex_f32", "alibi_slopes_recipe"):
         assert n in names
 
 
@@ -136,3 +137,58 @@ def test_python_binding_rejects_host_tensors():
         alibi.attn_fwd(x, x, x)
     with pytest.raises(ValueError):
         alibi.attn_decode(x[:, :, 0], x, x)
+
+
+@pytest.mark.parametrize("recipe", ["steep", "safe", "wide", "explicit"])
+@pytest.mark.parametrize("log_distance", [False, True])
+def test_host_slope_recipes_bitwise_equal_oracle(recipe, log_distance):
+    import alibi_linear_position_amd as alibi
+    for H in (1, 2, 3, 8, 9, 12, 16, 32, 64):
+        got = alibi.slopes_recipe(recipe, H, log_distance).numpy()
+        want = oracle.slopes_recipe_ref(recipe, H, log_distance)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (recipe, H)
+
+
+def test_default_recipe_is_the_geometric_schedule():
+    import alibi_linear_position_amd as alibi
+    for H in (4, 9, 16):
+        for log_distance in (False, True):
+            got = alibi.slopes_recipe("default", H, log_distance).numpy()
+            assert np.array_equal(got.view(np.uint32), oracle.slopes_ref(H).view(np.uint32))
+
+
+def test_slope_recipe_errors(lib):
+    buf = (ctypes.c_float * 8)()
+    assert lib.alibi_slopes_recipe(1, 0, 0, buf) == -1
+    assert lib.alibi_slopes_recipe(9, 4, 0, buf) == -1
+    assert lib.alibi_slopes_recipe(1, 4, 0, None) == -1
+
+
+def _fwd_ex(lib, fn="alibi_attn_fwd_ex", Nq=8, Nk=8, d=64, causal=1, opts=None, **kw):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, s=FAKE)
+    p.update(kw)
+    return getattr(lib, fn)(p["q"], p["k"], p["v"], p["o"], 1, 1, Nq, Nk, d, p["s"], causal,
+                            None if opts is None else ctypes.byref(opts), None)
+
+
+def test_fwd_ex_validation(lib):
+    import alibi_linear_position_amd as alibi
+    O = alibi.FwdOpts
+    assert _fwd_ex(lib, Nk=0) == -1
+    assert _fwd_ex(lib, Nq=0) == -1
+    assert _fwd_ex(lib, Nk=(1 << 24) + 1) == -1
+    assert _fwd_ex(lib, k=None) == -1
+    assert _fwd_ex(lib, causal=2) == -1
+    assert _fwd_ex(lib, opts=O(8, 0.0, 0.0, 0, 0)) == -1                 # unknown flag bit
+    assert _fwd_ex(lib, opts=O(1, float("nan"), 0.0, 0, 0)) == -1        # clamp not finite
+    assert _fwd_ex(lib, opts=O(1, float("-inf"), 0.0, 0, 0)) == -1
+    assert _fwd_ex(lib, opts=O(4, 0.0, 0.0, 0, 0)) == -1                 # soft cap must be > 0
+    assert _fwd_ex(lib, opts=O(4, 0.0, -50.0, 0, 0)) == -1
+    assert _fwd_ex(lib, opts=O(4, 0.0, float("inf"), 0, 0)) == -1
+    assert _fwd_ex(lib, opts=O(0, 0.0, 0.0, -1, 0)) == -1                # offsets 0 .. 2^24
+    assert _fwd_ex(lib, opts=O(0, 0.0, 0.0, 0, (1 << 24) + 1)) == -1
+    assert _fwd_ex(lib, d=264) == -2
+    assert _fwd_ex(lib, q=FAKE + 8) == -1
+    assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", q=FAKE + 2, d=16) == -1
+    assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", d=300) == -2
+    assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", opts=O(16, 0.0, 0.0, 0, 0), d=16) == -1
