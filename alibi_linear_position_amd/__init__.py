@@ -43,7 +43,7 @@ EXPORTS = {
 }
 
 # mitigation bits of alibi_fwd_opts.flags and the slope recipes (include/alibi.h)
-CLAMP, LOG_DISTANCE, SOFTCAP = 1, 2, 4
+CLAMP, LOG_DISTANCE, SOFTCAP, SKIP_UNDERFLOW = 1, 2, 4, 8
 RECIPES = {"default": 0, "steep": 1, "safe": 2, "wide": 3, "explicit": 4}
 
 
@@ -168,13 +168,14 @@ def attn_fwd_f32(q, k, v, slopes=None, causal=True, out=None):
 
 
 def attn_fwd_ex(q, k, v, slopes=None, causal=True, clamp=None, log_distance=False, softcap=None,
-                q_offset=0, k_offset=0, out=None):
+                q_offset=0, k_offset=0, skip_underflow=False, out=None):
     """Forward with mitigations and position offsets.
 
     q: (B, H, Nq, d); k, v: (B, H, Nk, d); bf16 (MFMA / generic kernel) or fp32
     (generic kernel), by q's dtype. clamp: bias floor or None; log_distance:
     ln(D + 1) distances; softcap: z or None; query row r sits at position
-    q_offset + r, key row c at k_offset + c.
+    q_offset + r, key row c at k_offset + c. skip_underflow: exact skipping of
+    key tiles whose weights all round to zero (bit-identical output).
     """
     import torch
     dtype = q.dtype
@@ -193,7 +194,7 @@ def attn_fwd_ex(q, k, v, slopes=None, causal=True, clamp=None, log_distance=Fals
         _need(out, dtype, 4, "out")
     o = FwdOpts()
     o.flags = (CLAMP if clamp is not None else 0) | (LOG_DISTANCE if log_distance else 0) | \
-        (SOFTCAP if softcap is not None else 0)
+        (SOFTCAP if softcap is not None else 0) | (SKIP_UNDERFLOW if skip_underflow else 0)
     o.clamp_min = float(clamp) if clamp is not None else 0.0
     o.softcap = float(softcap) if softcap is not None else 0.0
     o.q_offset = int(q_offset)

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -54,7 +55,8 @@ int check_fwd(const void* q, const void* k, const void* v, const void* out, cons
   if (causal != 0 && causal != 1) return ALIBI_EINVAL;
   *opt = alibi::FwdOptions{};
   if (opts != nullptr) {
-    if ((opts->flags & ~(ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP)) != 0) return ALIBI_EINVAL;
+    if ((opts->flags & ~(ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP | ALIBI_SKIP_UNDERFLOW)) != 0)
+      return ALIBI_EINVAL;
     if ((opts->flags & ALIBI_CLAMP) && !std::isfinite(opts->clamp_min)) return ALIBI_EINVAL;
     if ((opts->flags & ALIBI_SOFTCAP) && !(std::isfinite(opts->softcap) && opts->softcap > 0.0f))
       return ALIBI_EINVAL;
@@ -72,22 +74,26 @@ int check_fwd(const void* q, const void* k, const void* v, const void* out, cons
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ALIBI_OK : ALIBI_EHIP; }
 
-// ---- decode workspace: one growable buffer per device ----
+// ---- library workspaces: growable buffers per device ----
+// kDecode holds the decode's partial softmax states, kNorm the key-norm maxima
+// of the skipping forward. Both are used asynchronously on the caller's stream.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
+enum { kDecode = 0, kNorm = 1, kNumWorkspaces = 2 };
 std::mutex g_ws_mutex;
-std::vector<Workspace> g_ws;
+std::vector<Workspace> g_ws[kNumWorkspaces];
 
-int workspace_get(size_t bytes, float** out) {
+int workspace_get(int which, size_t bytes, float** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ALIBI_EHIP;
-  if ((size_t)dev >= g_ws.size()) g_ws.resize(dev + 1);
-  Workspace& w = g_ws[dev];
+  std::vector<Workspace>& list = g_ws[which];
+  if ((size_t)dev >= list.size()) list.resize(dev + 1);
+  Workspace& w = list[dev];
   if (w.bytes < bytes) {
     if (w.ptr) {
-      // an earlier asynchronous decode may still read the old buffer
+      // an earlier asynchronous call may still read the old buffer
       if (hipDeviceSynchronize() != hipSuccess) return ALIBI_EHIP;
       if (hipFree(w.ptr) != hipSuccess) return ALIBI_EHIP;
       w.ptr = nullptr;
@@ -137,6 +143,22 @@ int alibi_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, in
   if (d > 256 || d % 8 != 0) return ALIBI_ENOTSUP;
   const alibi::FwdArgs a{q, k, v, out, B, H, Nq, Nk, d, slopes, causal};
   if (d == 64 || d == 128) {
+    // Exact underflow skipping applies to the plain causal form; elsewhere the
+    // flag changes nothing (skipping is exact, so ignoring it is too).
+    const bool mitigated = (opt.flags & (ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP)) != 0;
+    if ((opt.flags & ALIBI_SKIP_UNDERFLOW) && causal && !mitigated) {
+      const int parts = std::max(1, std::min(std::max(1, Nk / 256), (2048 + B * H - 1) / (B * H)));
+      float* ws = nullptr;
+      {
+        std::lock_guard<std::mutex> lock(g_ws_mutex);
+        st = workspace_get(kNorm, (size_t)B * H * parts * sizeof(float), &ws);
+      }
+      if (st != ALIBI_OK) return st;
+      st = hip_status(alibi::launch_knorm_max(k, ws, B, H, Nk, d, parts, stream));
+      if (st != ALIBI_OK) return st;
+      opt.knorm = ws;
+      opt.knorm_parts = parts;
+    }
     if (log_enabled())
       std::fprintf(stderr, "[alibi] fwd mfma B=%d H=%d Nq=%d Nk=%d d=%d causal=%d flags=%d offsets=%d,%d\n",
                    B, H, Nq, Nk, d, causal, opt.flags, opt.q_offset, opt.k_offset);
@@ -191,7 +213,7 @@ int alibi_attn_decode(const void* q, const void* kcache, const void* vcache, voi
   if (splits > 1) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     const size_t bytes = (size_t)B * H * splits * (d + 2) * sizeof(float);
-    st = workspace_get(bytes, &ws);
+    st = workspace_get(kDecode, bytes, &ws);
     if (st != ALIBI_OK) return st;
   }
   if (log_enabled())
@@ -224,16 +246,20 @@ int alibi_release(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   int st = ALIBI_OK;
   int cur = 0;
-  if (!g_ws.empty() && hipGetDevice(&cur) != hipSuccess) return ALIBI_EHIP;
-  for (size_t dev = 0; dev < g_ws.size(); ++dev) {
-    if (!g_ws[dev].ptr) continue;
-    if (hipSetDevice(int(dev)) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-        hipFree(g_ws[dev].ptr) != hipSuccess)
-      st = ALIBI_EHIP;
-    g_ws[dev].ptr = nullptr;
-    g_ws[dev].bytes = 0;
+  bool any = false;
+  for (auto& list : g_ws) any = any || !list.empty();
+  if (any && hipGetDevice(&cur) != hipSuccess) return ALIBI_EHIP;
+  for (auto& list : g_ws) {
+    for (size_t dev = 0; dev < list.size(); ++dev) {
+      if (!list[dev].ptr) continue;
+      if (hipSetDevice(int(dev)) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+          hipFree(list[dev].ptr) != hipSuccess)
+        st = ALIBI_EHIP;
+      list[dev].ptr = nullptr;
+      list[dev].bytes = 0;
+    }
   }
-  if (!g_ws.empty()) (void)hipSetDevice(cur);
+  if (any) (void)hipSetDevice(cur);
   return st;
 }
 

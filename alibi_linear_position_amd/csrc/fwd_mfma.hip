@@ -171,7 +171,16 @@ struct FwdVariant {
   float clamp2;   // bias floor c_clamp log2(e)
   float cap_in;   // 2 log2(e) / (sqrt(d) z): exp2(s cap_in) = e^(2 A / z) for s = q.k
   float cap_out;  // z log2(e)
+  // Exact underflow skipping (plain causal form only): `parts` partial maxima
+  // of the key norms of each (b, h), or null.
+  const float* knorm;
+  int parts;
 };
+
+// A score whose exponent lies more than this many log2 units below the row's
+// running maximum gives p < 2^-134, which rounds to zero in bf16 (the smallest
+// subnormal is 2^-133); the skipping bound uses 140 plus the lazy-rescale lag.
+constexpr float kDeadLog2 = 140.0f + kLazy;
 
 template <int D, int NW, bool CAUSAL, int VAR>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
@@ -266,6 +275,50 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     regs.template store<KPITCH, VPITCH>(smem, smem + KBYTES, tid);
   }
 
+  // ---- exact underflow skipping ----
+  // For row i, every score against key j is at most A_i + c2 (j - pi) with
+  // A_i = |q_i| max_j |k_j| c1 (Cauchy-Schwarz), and the row's running maximum
+  // after its diagonal tile is at least its nearest visible key's score minus
+  // the lazy lag: >= -A_i - c2 max(0, pi - Nk + 1) - kLazy. A tile whose last
+  // key j_max has c2 (pi - j_max) > 140 + kLazy + 2 A_i + c2 max(0, pi - Nk + 1)
+  // therefore holds only p that round to exactly zero: skipping it leaves the
+  // output bit for bit unchanged. Tiles are visited from the diagonal backwards
+  // and the bound only grows with the distance, so everything at or below a
+  // wave's first dead tile is dead; the workgroup stops at the lowest tile any
+  // of its waves still needs, and a wave skips its own dead tiles before that.
+  __shared__ int s_dead[NW];
+  int t_dead_wave = -1, t_dead = -1;
+  if (CAUSAL && VAR == 0 && var.knorm != nullptr && c2 > 0.0f) {
+    float kmax = 0.0f;
+    for (int p = 0; p < var.parts; ++p) kmax = fmaxf(kmax, var.knorm[(long long)bh * var.parts + p]);
+    float qn2 = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 raw = __builtin_bit_cast(u32x4, qf[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf16lo_to_f32(raw[e]), b = bf16hi_to_f32(raw[e]);
+        qn2 = fmaf(a, a, fmaf(b, b, qn2));
+      }
+    }
+    // norms and their product carry a relative margin of 2^-8 against rounding
+    const float A = sqrtf(sum_xor32(qn2)) * kmax * c1 * (1.0f + 1.0f / 256.0f);
+    const float reach_f = (kDeadLog2 + 2.0f * A) / c2 + 1.0f;
+    const int reach = reach_f < 1.0e9f ? int(reach_f) + max(0, pi - Nk + 1) : (1 << 30);
+    const int x = pi - reach;                                   // dead: j_max < x
+    int td = x >= 0 ? x / BN - 1 : -1;                           // last tile with j_max < x
+    if (i >= Nq) td = 1 << 30;                                   // rows past Nq do not count
+    td = min(td, __shfl_xor(td, 32, 64));
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) td = min(td, __shfl_xor(td, off, 64));
+    t_dead_wave = max(__builtin_amdgcn_readfirstlane(td), -1);
+    if (lane == 0) s_dead[wave] = t_dead_wave;
+    __syncthreads();
+    t_dead = s_dead[0];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) t_dead = min(t_dead, s_dead[w2]);
+  }
+
   // Exponent of one score (log2 units) for the variants, from the plain
   // content score s = q.k and the signed distance pi - j (an exact integer).
   auto variant_t = [&](float s, float dist) {
@@ -302,7 +355,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const unsigned char* sV = sK + KBYTES;
     unsigned char* const sKn = smem + (stage ^ 1) * STAGE;
     stage ^= 1;
-    if (MASKED && !(qw0 < Nq && (!CAUSAL || j0 <= qw_last + delta))) {
+    if ((MASKED && !(qw0 < Nq && (!CAUSAL || j0 <= qw_last + delta))) || (!MASKED && tile <= t_dead_wave)) {
       regs.template store<KPITCH, VPITCH>(sKn, sKn + KBYTES, tid);
       return;
     }
@@ -411,7 +464,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   }
   int tile = ntiles - 1;
   for (; tile > t_open; --tile) step(tile, std::true_type{});
-  for (; tile >= 0; --tile) step(tile, std::false_type{});
+  for (; tile > t_dead; --tile) step(tile, std::false_type{});
 
   // ---- epilogue: O / l -> bf16; a row that saw no key gives 0 ----
   const float lt = sum_xor32(l_run);
@@ -465,7 +518,9 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hi
   const double z = opt.softcap > 0.0f ? double(opt.softcap) : 1.0;
   var.cap_in = float(2.0 * double(c1) / z);
   var.cap_out = float(z * 1.4426950408889634);
-  const int flags = opt.flags & 7;
+  var.knorm = opt.knorm;
+  var.parts = opt.knorm_parts;
+  const int flags = opt.flags & 7;  // the mitigation bits; skipping is a run-time argument
   if (a.d == 128)
     return a.causal ? launch_var<128, true>(a, flags, c1, var, stream)
                     : launch_var<128, false>(a, flags, c1, var, stream);

@@ -30,6 +30,10 @@ struct FwdOptions {
   float softcap = 0.0f;
   int q_offset = 0;
   int k_offset = 0;
+  // exact underflow skipping: P partial maxima of the key norms per (b, h)
+  // (launch_knorm_max), or null for no skipping
+  const float* knorm = nullptr;
+  int knorm_parts = 0;
 };
 
 // Generic (VALU) forward, any d <= 256: fp32 (f32 = true) or bf16 data.
@@ -37,6 +41,11 @@ hipError_t launch_fwd_generic(const FwdArgs& a, const FwdOptions& opt, bool f32,
 
 // MFMA forward, bf16, d in {64, 128}.
 hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hipStream_t stream);
+
+// Largest key norm of each (b, h) of k (B, H, N, d) bf16, d in {64, 128}, as P
+// partial maxima: out[(b H + h) P + p].
+hipError_t launch_knorm_max(const void* k, float* out, int B, int H, int N, int d, int P,
+                            hipStream_t stream);
 
 // Split-KV decode. `splits` key ranges of `chunk` keys each; ws holds
 // B*H*splits*(d+2) floats when splits > 1 (may be null when splits == 1).

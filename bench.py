@@ -11,6 +11,17 @@ the timed steps); the decode's GB/s (K + V + q + out bytes over its own event
 time) is reported under "decode". Both carry a roofline object against the
 MI355X datasheet peaks (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).
 
+After the timed steps, "next" reports the forward's other forms on the same
+inputs, each timed on its own (HIP events, after its own warmup): the Sec. 3.4
+mitigations of "When Attention Goes Blind" (bias floor -87, ln(D + 1)
+distances, soft cap 50; singly and all together), the symmetric non-causal
+bias, a chunked prefill (the last 512 query rows against the 4096-key
+cache through position offsets), and the exact underflow skipping (its rate
+counts the unskipped causal flops, so it is an effective rate, reported apart
+from the headline). Their flops are the algorithmic ones of each
+form: the causal triangle for the mitigations, N^2 without the mask, and the
+visible keys of the 512 rows for the prefill.
+
 The CPU baseline is the fp64 oracle itself, timed on this host's cores on a
 bounded sample (whole heads of the same forward, whole (b, h) pairs of the
 same decode), scaled to the same units.
@@ -111,7 +122,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None)
     args = ap.parse_args()
@@ -201,9 +212,58 @@ def main():
                                 "per_launch": f"{nbytes:.4e} B"}},
         "cpu_baseline": None,
     }
+    res["next"] = next_forms(alibi, qg, kg, vg, s_f, fw)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(q, k, v, kc, vc, qd, fw, dw)
     print(json.dumps(res), flush=True)
+
+
+def time_launches(fn, warmup=10, reps=10):
+    """Mean ms per call of fn over `reps` calls after `warmup` calls (HIP events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def next_forms(alibi, q, k, v, s, fw):
+    """TFLOP/s of the forward's mitigation, non-causal and chunked-prefill forms."""
+    import torch
+    B, H, N, d = fw.B, fw.H, fw.N, fw.d
+    causal_flops = fwd_flops(B, H, N, d)
+    out = torch.empty_like(q)
+    forms = {
+        "clamp": dict(clamp=-87.0),
+        "log_distance": dict(log_distance=True),
+        "softcap": dict(softcap=50.0),
+        "clamp+log+softcap": dict(clamp=-87.0, log_distance=True, softcap=50.0),
+    }
+    res = {}
+    for name, kw in forms.items():
+        ms = time_launches(lambda: alibi.attn_fwd_ex(q, k, v, s, True, out=out, **kw))
+        res[name] = {"value": round(causal_flops / ms / 1e9, 1), "unit": "TFLOP/s", "ms": round(ms, 4)}
+    ms = time_launches(lambda: alibi.attn_fwd(q, k, v, s, causal=False, out=out))
+    res["non_causal"] = {"value": round(4.0 * d * B * H * N * N / ms / 1e9, 1), "unit": "TFLOP/s",
+                         "ms": round(ms, 4)}
+    ms = time_launches(lambda: alibi.attn_fwd_ex(q, k, v, s, True, skip_underflow=True, out=out))
+    res["skip_underflow"] = {"value": round(causal_flops / ms / 1e9, 1), "unit": "TFLOP/s (causal flops)",
+                             "ms": round(ms, 4),
+                             "note": "exact skipping of all-underflow key tiles; key-norm pass included; "
+                                     "flops are the unskipped causal count, so this is not the headline"}
+    nq = 512
+    qc = q[:, :, N - nq:].contiguous()
+    oc = torch.empty_like(qc)
+    ms = time_launches(lambda: alibi.attn_fwd_ex(qc, k, v, s, True, q_offset=N - nq, out=oc))
+    vis = sum(N - nq + r + 1 for r in range(nq))
+    res["chunked_prefill_512_of_4096"] = {"value": round(4.0 * d * B * H * vis / ms / 1e9, 1),
+                                          "unit": "TFLOP/s", "ms": round(ms, 4)}
+    return res
 
 
 def run_only(args, alibi, W, fw, dw, dev):

@@ -101,7 +101,9 @@ int alibi_attn_fwd_f32(const float* q, const float* k, const float* v, float* ou
  * by a second kernel through a library-owned per-device workspace (see
  * alibi_release). Errors: as alibi_attn_fwd; ALIBI_ENOMEM if the workspace
  * cannot be allocated. Calls on one device are serialised by a mutex while
- * they size the workspace; the work itself stays asynchronous.
+ * they size the workspace; the work itself stays asynchronous, and every
+ * decode on one device uses the same workspace: order such calls on one
+ * stream (or synchronise between them).
  */
 int alibi_attn_decode(const void* q, const void* kcache, const void* vcache, void* out,
                       int B, int H, int L, int d, const float* slopes,
@@ -131,9 +133,23 @@ int alibi_attn_weights_f32(const float* q, const float* k, float* w,
 #define ALIBI_CLAMP 1
 #define ALIBI_LOG_DISTANCE 2
 #define ALIBI_SOFTCAP 4
+/*
+ * ALIBI_SKIP_UNDERFLOW: exact skipping of key tiles whose every weight would
+ * round to zero ("When Attention Goes Blind": the underflow of Sec. 3.2-3.3
+ * and the wasted work of Sec. 5.1-5.2). A first pass stores max_j |k_j| per
+ * (b, h) in a library-owned per-device workspace; the forward then bounds each
+ * score by |q_i| max|k| / sqrt(d) - m (i - j) and stops, per workgroup, at the
+ * first key tile where that bound lies more than 148 log2 units under the
+ * row's guaranteed running maximum. The output is bit-identical to the call
+ * without the flag. It acts on the plain causal form with d in {64, 128}; with
+ * mitigations, without the causal mask or on the generic kernel it is accepted
+ * and changes nothing. Calls with this flag on one device share the workspace:
+ * order them on one stream (or synchronise between them).
+ */
+#define ALIBI_SKIP_UNDERFLOW 8
 
 typedef struct alibi_fwd_opts {
-  int flags;         /* OR of the ALIBI_* mitigation bits; other bits -> ALIBI_EINVAL */
+  int flags;         /* OR of the ALIBI_* bits above; other bits -> ALIBI_EINVAL */
   float clamp_min;   /* bias floor in logit units (e.g. -87); finite; used with ALIBI_CLAMP */
   float softcap;     /* z > 0, finite (e.g. 50); used with ALIBI_SOFTCAP */
   int q_offset;      /* position of query row 0, 0 .. 2^24 */

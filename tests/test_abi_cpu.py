@@ -179,7 +179,7 @@ def test_fwd_ex_validation(lib):
     assert _fwd_ex(lib, Nk=(1 << 24) + 1) == -1
     assert _fwd_ex(lib, k=None) == -1
     assert _fwd_ex(lib, causal=2) == -1
-    assert _fwd_ex(lib, opts=O(8, 0.0, 0.0, 0, 0)) == -1                 # unknown flag bit
+    assert _fwd_ex(lib, opts=O(16, 0.0, 0.0, 0, 0)) == -1                # unknown flag bit
     assert _fwd_ex(lib, opts=O(1, float("nan"), 0.0, 0, 0)) == -1        # clamp not finite
     assert _fwd_ex(lib, opts=O(1, float("-inf"), 0.0, 0, 0)) == -1
     assert _fwd_ex(lib, opts=O(4, 0.0, 0.0, 0, 0)) == -1                 # soft cap must be > 0
