@@ -23,3 +23,6 @@ from .underflow import (  # noqa: F401
 from .mitigations import (  # noqa: F401
     TAU_D, recipe_distances, slopes_recipe_ref, variant_head_ref, variant_ref,
 )
+from .backward import (  # noqa: F401
+    lse_head_ref, lse_ref, attn_backward_head_ref, attn_backward_ref,
+)

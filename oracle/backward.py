@@ -1,0 +1,77 @@
+"""Gradients of ALiBi attention in plain fp64 (test infrastructure, not the product).
+
+The pages define the forward only: out = softmax(Q K^T / sqrt(d) + B) V with
+the fixed ALiBi bias B = -m (i - j) and the causal mask ("When Attention Goes
+Blind", Sec. 3.1 Eq. 1-3; the slopes are fixed, not learned: abhik.ai,
+"Different heads, different distance penalties"). Sec. 4.2 / 5.1 of the
+paper train such models and discuss what underflow does to the backward
+pass, which is the reason the gradients are on the hot path here.
+
+The gradients below are the chain rule of that definition, step by step:
+  P = softmax(logits), O = P V
+  dV = P^T dO
+  dP = dO V^T
+  dS = P * (dP - rowsum(P * dP))      (the softmax Jacobian applied row by row)
+  dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d)
+The bias is a constant, so it has no gradient of its own. The row log-sum-exp
+of the logits (natural log) is what a forward pass keeps for this backward.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .alibi_ref import _f64, bias_ref, distance_ref, softmax_rows_ref
+
+
+def _logits(q, k, m, causal):
+    a = (q @ k.T) / math.sqrt(q.shape[-1])
+    dist = distance_ref(q.shape[0], k.shape[0])
+    logits = a + bias_ref(m, dist, causal)
+    if causal:
+        logits = np.where(dist < 0, -np.inf, logits)
+    return logits
+
+
+def lse_head_ref(q, k, m, causal=True):
+    """Row log-sum-exp (natural log) of one head's logits, fp64."""
+    logits = _logits(_f64(q), _f64(k), m, causal)
+    mx = np.max(logits, axis=-1, keepdims=True)
+    return (mx + np.log(np.sum(np.exp(logits - mx), axis=-1, keepdims=True)))[:, 0]
+
+
+def attn_backward_head_ref(q, k, v, do, m, causal=True):
+    """(dq, dk, dv) of one head for the upstream gradient do, fp64."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    p = softmax_rows_ref(_logits(q, k, m, causal))
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+    scale = 1.0 / math.sqrt(q.shape[-1])
+    return ds @ k * scale, ds.T @ q * scale, dv
+
+
+def attn_backward_ref(q, k, v, do, slopes, causal=True):
+    """Multi-head gradients: inputs (B, H, N, d); returns dq, dk, dv (B, H, N, d) fp64."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    slopes = np.asarray(_f64(slopes)).reshape(-1)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            dq[b, h], dk[b, h], dv[b, h] = attn_backward_head_ref(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                                  slopes[h], causal)
+    return dq, dk, dv
+
+
+def lse_ref(q, k, slopes, causal=True):
+    """Row log-sum-exp (natural log), (B, H, N) fp64."""
+    q, k = _f64(q), _f64(k)
+    slopes = np.asarray(_f64(slopes)).reshape(-1)
+    out = np.empty(q.shape[:3], dtype=np.float64)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            out[b, h] = lse_head_ref(q[b, h], k[b, h], slopes[h], causal)
+    return out

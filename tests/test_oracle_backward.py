@@ -1,0 +1,98 @@
+"""Pins of the oracle's gradients and row log-sum-exp (CPU only).
+
+The gradients are tied to (i) PyTorch autograd through the forward definition
+in fp64 (torch's SDPA with the explicit ALiBi bias as an additive mask, a
+library routine standing in for the definition), (ii) central finite
+differences of the oracle's own, separately pinned, forward (no autograd), and
+(iii) closed forms the softmax fixes: the column sums of dV equal the sum of
+dO, dQ vanishes when all keys are equal, and adding one vector to every key
+changes no gradient. The log-sum-exp is tied to scipy and to the forward's
+weights (w = exp(logit - lse)).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _torch_grads(q, k, v, do, m, causal):
+    import torch
+    qt, kt, vt = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    n = q.shape[0]
+    i = torch.arange(n, dtype=torch.float64)[:, None]
+    j = torch.arange(n, dtype=torch.float64)[None, :]
+    bias = -m * (i - j) if causal else -m * (i - j).abs()
+    if causal:
+        bias = bias.masked_fill(j > i, float("-inf"))
+    out = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None], attn_mask=bias)[0]
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("m", [0.0, 0.0625, 0.7])
+def test_backward_matches_autograd(causal, m):
+    n, d = 23, 16
+    q, k, v, do = (_rand((n, d), s) for s in (1, 2, 3, 4))
+    got = oracle.attn_backward_head_ref(q, k, v, do, m, causal)
+    want = _torch_grads(q, k, v, do, m, causal)
+    for g, w in zip(got, want):
+        assert np.allclose(g, w, atol=1e-12, rtol=1e-10)
+
+
+def test_backward_matches_finite_differences():
+    n, d, m, eps = 6, 4, 0.3, 1e-6
+    q, k, v, do = (_rand((n, d), s, 0.7) for s in (5, 6, 7, 8))
+    dq, dk, dv = oracle.attn_backward_head_ref(q, k, v, do, m, True)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attn_head_ref(qq, kk, vv, m, True)
+        return float(np.sum(o * do))
+
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            plus = [q.copy(), k.copy(), v.copy()]
+            minus = [q.copy(), k.copy(), v.copy()]
+            plus[which][idx] += eps
+            minus[which][idx] -= eps
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * eps)
+        assert np.allclose(grad, num, atol=1e-7), which
+
+
+def test_dv_column_sum_equals_do_sum():
+    q, k, v, do = (_rand((17, 8), s) for s in (9, 10, 11, 12))
+    _, _, dv = oracle.attn_backward_head_ref(q, k, v, do, 0.25, True)
+    assert np.allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
+
+
+def test_dq_vanishes_for_equal_keys_and_key_shift_changes_nothing():
+    n, d = 12, 8
+    q, v, do = (_rand((n, d), s) for s in (13, 14, 15))
+    k_same = np.tile(_rand((1, d), 16), (n, 1))
+    dq, _, _ = oracle.attn_backward_head_ref(q, k_same, v, do, 0.5, True)
+    assert np.allclose(dq, 0.0, atol=1e-12)
+    k = _rand((n, d), 17)
+    g1 = oracle.attn_backward_head_ref(q, k, v, do, 0.5, True)
+    g2 = oracle.attn_backward_head_ref(q, k + _rand((1, d), 18), v, do, 0.5, True)
+    for a, b in zip(g1, g2):
+        assert np.allclose(a, b, atol=1e-11)
+
+
+def test_lse_against_scipy_and_weights():
+    from scipy.special import logsumexp
+    n, d, m = 20, 8, 0.4
+    q, k, v = (_rand((n, d), s) for s in (19, 20, 21))
+    lse = oracle.lse_head_ref(q, k, m, True)
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    logits = np.where(j <= i, q @ k.T / math.sqrt(d) - m * (i - j), -np.inf)
+    assert np.allclose(lse, logsumexp(logits, axis=1), atol=1e-12)
+    _, w = oracle.attn_head_ref(q, k, v, m, True)
+    assert np.allclose(np.where(j <= i, np.exp(logits - lse[:, None]), 0.0), w, atol=1e-13)
