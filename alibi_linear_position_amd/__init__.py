@@ -12,6 +12,8 @@ or a call returns an error status, these functions raise.
                 q_offset=, k_offset=)     -> mitigations / position offsets,
                                              bf16 or fp32 by q's dtype
     slopes_recipe(recipe, H, log_distance) -> float32 CPU tensor
+    attn_fwd_train(q, k, v, slopes, causal) -> (out, lse)
+    attn_bwd(q, k, v, out, dout, lse, slopes, causal) -> (dq, dk, dv)
     attn_decode(q, kcache, vcache, slopes)  -> bf16 (B, H, d)
     attn_weights_f32(q, k, slopes, causal)  -> fp32 (B, H, N, N), test only
 """
@@ -38,6 +40,7 @@ EXPORTS = {
     "alibi_attn_fwd_ex": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P],
     "alibi_attn_fwd_ex_f32": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P],
     "alibi_slopes_recipe": [_I, _I, _I, _P],
+    "alibi_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
     "alibi_status_string": [_I],
     "alibi_release": [],
 }
@@ -50,7 +53,7 @@ RECIPES = {"default": 0, "steep": 1, "safe": 2, "wide": 3, "explicit": 4}
 class FwdOpts(ctypes.Structure):
     """Mirror of struct alibi_fwd_opts."""
     _fields_ = [("flags", ctypes.c_int), ("clamp_min", ctypes.c_float), ("softcap", ctypes.c_float),
-                ("q_offset", ctypes.c_int), ("k_offset", ctypes.c_int)]
+                ("q_offset", ctypes.c_int), ("k_offset", ctypes.c_int), ("lse", ctypes.c_void_p)]
 
 
 _lib = None
@@ -168,14 +171,15 @@ def attn_fwd_f32(q, k, v, slopes=None, causal=True, out=None):
 
 
 def attn_fwd_ex(q, k, v, slopes=None, causal=True, clamp=None, log_distance=False, softcap=None,
-                q_offset=0, k_offset=0, skip_underflow=False, out=None):
+                q_offset=0, k_offset=0, skip_underflow=False, out=None, lse=None):
     """Forward with mitigations and position offsets.
 
     q: (B, H, Nq, d); k, v: (B, H, Nk, d); bf16 (MFMA / generic kernel) or fp32
     (generic kernel), by q's dtype. clamp: bias floor or None; log_distance:
     ln(D + 1) distances; softcap: z or None; query row r sits at position
     q_offset + r, key row c at k_offset + c. skip_underflow: exact skipping of
-    key tiles whose weights all round to zero (bit-identical output).
+    key tiles whose weights all round to zero (bit-identical output). lse: an
+    fp32 (B, H, Nq) device tensor that receives each row's log-sum-exp.
     """
     import torch
     dtype = q.dtype
@@ -199,6 +203,11 @@ def attn_fwd_ex(q, k, v, slopes=None, causal=True, clamp=None, log_distance=Fals
     o.softcap = float(softcap) if softcap is not None else 0.0
     o.q_offset = int(q_offset)
     o.k_offset = int(k_offset)
+    if lse is not None:
+        _need(lse, torch.float32, 3, "lse")
+        if tuple(lse.shape) != (B, H, Nq):
+            raise ValueError("lse must be (B, H, Nq)")
+        o.lse = lse.data_ptr()
     entry = "alibi_attn_fwd_ex" if dtype == torch.bfloat16 else "alibi_attn_fwd_ex_f32"
     with torch.cuda.device(q.device):
         st = getattr(load_library(), entry)(
@@ -207,6 +216,37 @@ def attn_fwd_ex(q, k, v, slopes=None, causal=True, clamp=None, log_distance=Fals
             _stream_handle(q.device))
     _check(entry, st)
     return out
+
+
+def attn_fwd_train(q, k, v, slopes=None, causal=True):
+    """Forward that also returns the row log-sum-exp the backward needs: (out, lse)."""
+    import torch
+    B, H, N, _ = q.shape
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    out = attn_fwd_ex(q, k, v, slopes, causal, lse=lse)
+    return out, lse
+
+
+def attn_bwd(q, k, v, out, dout, lse, slopes=None, causal=True):
+    """Gradients (dq, dk, dv), bf16 (B, H, N, d), of the plain forward."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, torch.bfloat16, 4, n)
+        if t.shape != q.shape:
+            raise ValueError(f"{n} must have q's shape")
+    _need(lse, torch.float32, 3, "lse")
+    B, H, N, d = q.shape
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be (B, H, N)")
+    s = _slopes_dev(slopes, H, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        st = load_library().alibi_attn_bwd(
+            _P(q.data_ptr()), _P(k.data_ptr()), _P(v.data_ptr()), _P(out.data_ptr()),
+            _P(dout.data_ptr()), _P(lse.data_ptr()), _P(dq.data_ptr()), _P(dk.data_ptr()),
+            _P(dv.data_ptr()), B, H, N, d, _P(s.data_ptr()), int(bool(causal)), _stream_handle(q.device))
+    _check("alibi_attn_bwd", st)
+    return dq, dk, dv
 
 
 def attn_decode(q, kcache, vcache, slopes=None, out=None):

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libalibi.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "fwd_generic.hip", "fwd_mfma.hip", "decode.hip", "knorm.hip"]
+SOURCES = ["api.cpp", "fwd_generic.hip", "fwd_mfma.hip", "decode.hip", "knorm.hip", "bwd.hip"]
 
 
 def hipcc() -> str:

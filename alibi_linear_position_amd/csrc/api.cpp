@@ -67,6 +67,8 @@ int check_fwd(const void* q, const void* k, const void* v, const void* out, cons
     opt->softcap = opts->softcap;
     opt->q_offset = opts->q_offset;
     opt->k_offset = opts->k_offset;
+    if (opts->lse != nullptr && !aligned(opts->lse, 4)) return ALIBI_EINVAL;
+    opt->lse = opts->lse;
   }
   if ((long long)B * H * Nk > (1LL << 31) * 4) return ALIBI_ENOTSUP;
   return ALIBI_OK;
@@ -76,12 +78,12 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ALIBI_OK : ALIBI_EHIP; }
 
 // ---- library workspaces: growable buffers per device ----
 // kDecode holds the decode's partial softmax states, kNorm the key-norm maxima
-// of the skipping forward. Both are used asynchronously on the caller's stream.
+// of the skipping forward, kBwd the backward's row terms. Both are used asynchronously on the caller's stream.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
-enum { kDecode = 0, kNorm = 1, kNumWorkspaces = 2 };
+enum { kDecode = 0, kNorm = 1, kBwd = 2, kNumWorkspaces = 3 };
 std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws[kNumWorkspaces];
 
@@ -177,6 +179,27 @@ int alibi_attn_fwd_ex_f32(const float* q, const float* k, const float* v, float*
   if (d > 256) return ALIBI_ENOTSUP;
   const alibi::FwdArgs a{q, k, v, out, B, H, Nq, Nk, d, slopes, causal};
   return hip_status(alibi::launch_fwd_generic(a, opt, true, stream));
+}
+
+int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   const float* slopes, int causal, hipStream_t stream) {
+  int st = check_common(q, k, v, out, slopes, B, H, N, d, 16);
+  if (st != ALIBI_OK) return st;
+  st = check_common(dout, dq, dk, dv, slopes, B, H, N, d, 16);
+  if (st != ALIBI_OK) return st;
+  if (lse == nullptr || !aligned(lse, 4)) return ALIBI_EINVAL;
+  if (causal != 0 && causal != 1) return ALIBI_EINVAL;
+  if (d != 64 && d != 128) return ALIBI_ENOTSUP;
+  float* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    st = workspace_get(kBwd, (size_t)2 * B * H * N * sizeof(float), &ws);
+  }
+  if (st != ALIBI_OK) return st;
+  if (log_enabled()) std::fprintf(stderr, "[alibi] bwd B=%d H=%d N=%d d=%d causal=%d\n", B, H, N, d, causal);
+  const alibi::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, slopes, causal};
+  return hip_status(alibi::launch_bwd(a, ws, scale_log2(d), stream));
 }
 
 int alibi_slopes_recipe(int recipe, int H, int log_distance, float* slopes_out) {

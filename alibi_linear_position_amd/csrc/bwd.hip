@@ -1,0 +1,486 @@
+// Backward pass of ALiBi attention on gfx950 bf16 MFMA (d = 64 or 128).
+//
+// Gradients of out = softmax(Q K^T / sqrt(d) - m (i - j), causal mask) V with
+// respect to q, k and v (the bias is a constant: ALiBi slopes are fixed, not
+// learned -- abhik.ai, "Different heads, different distance penalties"). With
+// P_ij = exp(S_ij - lse_i) recomputed from the forward's row log-sum-exp:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = sum_d dO_i O_i,
+//   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d).
+// "When Attention Goes Blind" (Sec. 4.2, 5.1) trains ALiBi models and argues
+// that the underflowed weights matter most in exactly this pass.
+//
+// Three kernels:
+// * bwd_prep_kernel: D_i and the log-sum-exp in log2 units, one lane group
+//   per row.
+// * bwd_dkdv_kernel: one workgroup per 128 keys of one (b, h); each of its 4
+//   waves owns 32 keys and keeps their K and V rows as MFMA B operands in
+//   registers, and the dK^T, dV^T accumulators. Query tiles of 32 rows stream
+//   through LDS (double-buffered): Q and dO row-major for S = Q K^T and
+//   dP = dO V^T (rows = queries, lane = key), and transposed with the same key
+//   permutation as the forward's V^T for dV^T += dO^T P and dK^T += Q^T dS, so
+//   P and dS go from registers to the next MFMA as B operands.
+// * bwd_dq_kernel: one workgroup per 128 queries, the forward's layout:
+//   S^T = K Q^T and dP^T = V dO^T (lane = query, so lse and D are one value
+//   per lane), dS^T packed to bf16 and dQ^T += K^T dS^T; K row-major, K^T and
+//   V row-major staged per 64-key tile.
+// Scores are in log2 units (c1 = log2(e) / sqrt(d), c2 = m log2(e)); masked and
+// out-of-range entries get P = 0.
+#include "device_common.h"
+#include "launch.h"
+
+#include <cmath>
+
+namespace alibi {
+
+namespace {
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Position of index x (0..15) inside a 16-wide MFMA k-step whose B operand comes
+// from an accumulator: swaps 4-7 with 8-11.
+__device__ __forceinline__ int perm16(int x) { return ((x & 4) << 1) | ((x & 8) >> 1) | (x & 3); }
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Pack 8 fp32 values (registers base .. base + 7 of an accumulator) to bf16.
+__device__ __forceinline__ u32x4 pack8(const f32x16& x, int base) {
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(x[base + 2 * e], x[base + 2 * e + 1]);
+  return r;
+}
+
+// ---------------------------------------------------------------- prep ------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
+                                                       const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ dsum, float* __restrict__ lse2,
+                                                       long long rows) {
+  constexpr int LPR = D / 8;
+  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float s = 0.0f;
+  if (row < rows) {
+    const u32x4 a = load16(o + row * D + sub * 8), b = load16(dout + row * D + sub * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(bf16lo_to_f32(a[e]), bf16lo_to_f32(b[e]), s);
+      s = fmaf(bf16hi_to_f32(a[e]), bf16hi_to_f32(b[e]), s);
+    }
+  }
+  s = group_sum<LPR>(s);
+  if (row < rows && sub == 0) {
+    dsum[row] = s;
+    lse2[row] = lse[row] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV ----
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int H, int N, int nkb, int total,
+    const float* __restrict__ slopes, float c1, float scale) {
+  constexpr int NT = 256, BK = 128, BQ = 32;
+  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int RPITCH = D * 2 + 16;  // row-major Q / dO rows, bytes
+  constexpr int TPITCH = BQ * 2 + 16; // transposed [d][query], bytes
+  constexpr int RBYTES = BQ * RPITCH;
+  constexpr int TBYTES = D * TPITCH;
+  constexpr int STAGE = 2 * RBYTES + 2 * TBYTES + 2 * BQ * 4;
+  constexpr int LOADS = BQ * CPR / NT;  // 16-byte chunks of Q (and of dO) per thread
+  static_assert(LOADS * NT == BQ * CPR, "tile must split evenly");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int w = blockIdx.x;
+  const int lw = (total & 7) == 0 ? (w & 7) * (total >> 3) + (w >> 3) : w;
+  const int bh = lw / nkb;
+  const int kblk = lw - bh * nkb;  // low key blocks see the most queries: scheduled first
+  const int h = bh % H;
+  const float c2 = slopes[h] * kLog2e;
+  const float c21 = c2 / c1;
+  const long long base = (long long)bh * N * D;
+  const long long rbase = (long long)bh * N;
+  const int k0 = kblk * BK;
+  const int kw0 = k0 + wave * 32;
+  const int j = kw0 + l32;  // this lane's key
+
+  // K and V rows of this lane's key as B operands (k index = d).
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (j < N) {
+      a = load16(k + base + (long long)j * D + 16 * ks + 8 * hi);
+      b = load16(v + base + (long long)j * D + 16 * ks + 8 * hi);
+    }
+    kf[ks] = __builtin_bit_cast(bf16x8, a);
+    vf[ks] = __builtin_bit_cast(bf16x8, b);
+  }
+  // S rows are queries 8 (r / 4) + 4 hi + r % 4 of the tile; seeding register r
+  // with -c2 / c1 (8 (r / 4) + r % 4) leaves one fma for the bias.
+  f32x16 cinit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cinit[r] = -c21 * float(8 * (r >> 2) + (r & 3));
+
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? k0 / BQ : 0;
+
+  // staging registers of one query tile
+  u32x4 rq[LOADS], rdo[LOADS];
+  float rl = 0.0f, rd = 0.0f;
+  auto load_tile = [&](int qt) {
+    const int q0 = qt * BQ;
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int c = tid + NT * r, row = c / CPR, col = c % CPR;
+      rq[r] = u32x4{0u, 0u, 0u, 0u};
+      rdo[r] = u32x4{0u, 0u, 0u, 0u};
+      if (q0 + row < N) {
+        rq[r] = load16(q + base + (long long)(q0 + row) * D + col * 8);
+        rdo[r] = load16(dout + base + (long long)(q0 + row) * D + col * 8);
+      }
+    }
+    if (tid < BQ) {
+      const bool ok = q0 + tid < N;
+      rl = ok ? lse2[rbase + q0 + tid] : __builtin_huge_valf();  // rows past N: P = 0
+      rd = ok ? dsum[rbase + q0 + tid] : 0.0f;
+    }
+  };
+  auto store_tile = [&](unsigned char* st) {
+    unsigned char* sQ = st;
+    unsigned char* sO = st + RBYTES;
+    unsigned char* sQT = st + 2 * RBYTES;
+    unsigned char* sOT = sQT + TBYTES;
+    float* sL = reinterpret_cast<float*>(sOT + TBYTES);
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int c = tid + NT * r, row = c / CPR, col = c % CPR;
+      *reinterpret_cast<u32x4*>(sQ + row * RPITCH + col * 16) = rq[r];
+      *reinterpret_cast<u32x4*>(sO + row * RPITCH + col * 16) = rdo[r];
+      const int pos = (row & ~15) | perm16(row & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d0 = col * 8 + 2 * e;
+        *reinterpret_cast<uint16_t*>(sQT + d0 * TPITCH + pos * 2) = uint16_t(rq[r][e] & 0xffffu);
+        *reinterpret_cast<uint16_t*>(sQT + (d0 + 1) * TPITCH + pos * 2) = uint16_t(rq[r][e] >> 16);
+        *reinterpret_cast<uint16_t*>(sOT + d0 * TPITCH + pos * 2) = uint16_t(rdo[r][e] & 0xffffu);
+        *reinterpret_cast<uint16_t*>(sOT + (d0 + 1) * TPITCH + pos * 2) = uint16_t(rdo[r][e] >> 16);
+      }
+    }
+    if (tid < BQ) {
+      sL[tid] = rl;
+      sL[BQ + tid] = rd;
+    }
+  };
+
+  if (qt0 < nqt) {
+    load_tile(qt0);
+    store_tile(smem);
+  }
+  int stage = 0;
+  for (int qt = qt0; qt < nqt; ++qt, stage ^= 1) {
+    __syncthreads();
+    if (qt + 1 < nqt) load_tile(qt + 1);
+    const unsigned char* st = smem + stage * STAGE;
+    const unsigned char* sQ = st;
+    const unsigned char* sO = st + RBYTES;
+    const unsigned char* sQT = st + 2 * RBYTES;
+    const unsigned char* sOT = sQT + TBYTES;
+    const float* sL = reinterpret_cast<const float*>(sOT + TBYTES);
+    const int q0 = qt * BQ;
+    const bool active = !CAUSAL || q0 + BQ - 1 >= kw0;
+    if (active) {
+      // ---- S = Q K^T (rows = queries, lane = key), dP = dO V^T ----
+      f32x16 s = cinit, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + l32 * RPITCH + (16 * ks + 8 * hi) * 2);
+        s = mfma32(a, kf[ks], s);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sO + l32 * RPITCH + (16 * ks + 8 * hi) * 2);
+        dp = mfma32(a, vf[ks], dp);
+      }
+      // ---- P = exp2(t - lse2), dS = P (dP - D) ----
+      const float bj = c2 * float(j - q0 - 4 * hi);  // t = s c1 + bj on the causal side
+      const bool full = CAUSAL && q0 >= kw0 + 31;    // every query of the tile sees every key of the wave
+      f32x16 p, ds;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 L = *reinterpret_cast<const f32x4*>(sL + 8 * g + 4 * hi);
+        const f32x4 Dv = *reinterpret_cast<const f32x4*>(sL + BQ + 8 * g + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const int i = q0 + 8 * g + 4 * hi + e;
+          float t = fmaf(s[r], c1, bj);
+          if (!full) {
+            if (!CAUSAL && j > i) t -= 2.0f * c2 * float(j - i);  // symmetric bias -m |i - j|
+            if (CAUSAL && j > i) t = -__builtin_huge_valf();
+          }
+          const float pr = fast_exp2(t - L[e]);
+          p[r] = pr;
+          ds[r] = pr * (dp[r] - Dv[e]);
+        }
+      }
+      const u32x4 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
+      const u32x4 sb0 = pack8(ds, 0), sb1 = pack8(ds, 8);
+      // ---- dV^T += dO^T P, dK^T += Q^T dS ----
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const unsigned char* ro = sOT + (32 * db + l32) * TPITCH + 8 * hi * 2;
+        const unsigned char* rq2 = sQT + (32 * db + l32) * TPITCH + 8 * hi * 2;
+        dva[db] = mfma32(*reinterpret_cast<const bf16x8*>(ro), __builtin_bit_cast(bf16x8, pb0), dva[db]);
+        dva[db] = mfma32(*reinterpret_cast<const bf16x8*>(ro + 32), __builtin_bit_cast(bf16x8, pb1), dva[db]);
+        dka[db] = mfma32(*reinterpret_cast<const bf16x8*>(rq2), __builtin_bit_cast(bf16x8, sb0), dka[db]);
+        dka[db] = mfma32(*reinterpret_cast<const bf16x8*>(rq2 + 32), __builtin_bit_cast(bf16x8, sb1), dka[db]);
+      }
+    }
+    if (qt + 1 < nqt) store_tile(smem + (stage ^ 1) * STAGE);
+  }
+
+  // ---- epilogue: lane = key j, rows of the accumulators = d ----
+  if (j < N) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const long long off = base + (long long)j * D + 32 * db + 8 * g + 4 * hi;
+        u32x2 a, b;
+        a[0] = pack_bf16x2(dka[db][4 * g] * scale, dka[db][4 * g + 1] * scale);
+        a[1] = pack_bf16x2(dka[db][4 * g + 2] * scale, dka[db][4 * g + 3] * scale);
+        b[0] = pack_bf16x2(dva[db][4 * g], dva[db][4 * g + 1]);
+        b[1] = pack_bf16x2(dva[db][4 * g + 2], dva[db][4 * g + 3]);
+        *reinterpret_cast<u32x2*>(dk + off) = a;
+        *reinterpret_cast<u32x2*>(dv + off) = b;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ --------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
+    uint16_t* __restrict__ dq, int H, int N, int nqb, int total, const float* __restrict__ slopes,
+    float c1, float scale) {
+  constexpr int NT = 256, BM = 128, BN = 64;
+  constexpr int KS = D / 16, KB = BN / 32, DB = D / 32, PS = BN / 16, CPR = D / 8;
+  constexpr int KPITCH = D * 2 + 16;   // K and V rows, bytes
+  constexpr int TPITCH = BN * 2 + 16;  // K^T [d][key], bytes
+  constexpr int KBYTES = BN * KPITCH;
+  constexpr int STAGE = 2 * KBYTES + D * TPITCH;
+  constexpr int LOADS = BN * CPR / NT;
+  static_assert(LOADS * NT == BN * CPR, "tile must split evenly");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int w = blockIdx.x;
+  const int lw = (total & 7) == 0 ? (w & 7) * (total >> 3) + (w >> 3) : w;
+  const int bh = lw / nqb;
+  const int qblk = nqb - 1 - (lw - bh * nqb);
+  const int h = bh % H;
+  const float c2 = slopes[h] * kLog2e;
+  const float c21 = c2 / c1;
+  const long long base = (long long)bh * N * D;
+  const long long rbase = (long long)bh * N;
+  const int q0 = qblk * BM;
+  const int qw0 = q0 + wave * 32;
+  const int qw_last = min(qw0 + 32, N) - 1;
+  const int i = qw0 + l32;
+
+  bf16x8 qf[KS], of[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (i < N) {
+      a = load16(q + base + (long long)i * D + 16 * ks + 8 * hi);
+      b = load16(dout + base + (long long)i * D + 16 * ks + 8 * hi);
+    }
+    qf[ks] = __builtin_bit_cast(bf16x8, a);
+    of[ks] = __builtin_bit_cast(bf16x8, b);
+  }
+  const float L = i < N ? lse2[rbase + i] : __builtin_huge_valf();
+  const float Dr = i < N ? dsum[rbase + i] : 0.0f;
+  f32x16 cinit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cinit[r] = c21 * float(8 * (r >> 2) + (r & 3));
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  // K chunks go one key per lane (so the transposed writes of a wave cover
+  // whole 16-key groups), V chunks row-major.
+  u32x4 rk[LOADS], rv[LOADS];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int key = tid % BN, col = tid / BN + (NT / BN) * r;
+      rk[r] = u32x4{0u, 0u, 0u, 0u};
+      if (j0 + key < N) rk[r] = load16(k + base + (long long)(j0 + key) * D + col * 8);
+      const int c = tid + NT * r, row = c / CPR, vc = c % CPR;
+      rv[r] = u32x4{0u, 0u, 0u, 0u};
+      if (j0 + row < N) rv[r] = load16(v + base + (long long)(j0 + row) * D + vc * 8);
+    }
+  };
+  auto store_tile = [&](unsigned char* st) {
+    unsigned char* sK = st;
+    unsigned char* sV = st + KBYTES;
+    unsigned char* sKT = st + 2 * KBYTES;
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int key = tid % BN, col = tid / BN + (NT / BN) * r;
+      *reinterpret_cast<u32x4*>(sK + key * KPITCH + col * 16) = rk[r];
+      const int pos = (key & ~15) | perm16(key & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint16_t*>(sKT + (col * 8 + 2 * e) * TPITCH + pos * 2) = uint16_t(rk[r][e] & 0xffffu);
+        *reinterpret_cast<uint16_t*>(sKT + (col * 8 + 2 * e + 1) * TPITCH + pos * 2) = uint16_t(rk[r][e] >> 16);
+      }
+      const int c = tid + NT * r, row = c / CPR, vc = c % CPR;
+      *reinterpret_cast<u32x4*>(sV + row * KPITCH + vc * 16) = rv[r];
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile((ntiles - 1) * BN);
+    store_tile(smem);
+  }
+  int stage = 0;
+  for (int tile = ntiles - 1; tile >= 0; --tile, stage ^= 1) {
+    const int j0 = tile * BN;
+    __syncthreads();
+    if (tile > 0) load_tile(j0 - BN);
+    const unsigned char* st = smem + stage * STAGE;
+    const unsigned char* sK = st;
+    const unsigned char* sV = st + KBYTES;
+    const unsigned char* sKT = st + 2 * KBYTES;
+    const bool active = qw0 < N && (!CAUSAL || j0 <= qw_last);
+    if (active) {
+      // ---- S^T = K Q^T, dP^T = V dO^T (lane = query) ----
+      f32x16 s[KB], dp[KB];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
+          s[kb] = mfma32(a, qf[ks], ks == 0 ? cinit : s[kb]);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(sV + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
+          dp[kb] = mfma32(b, of[ks], ks == 0 ? f32x16{} : dp[kb]);
+        }
+      }
+      // ---- P^T = exp2(t - lse2), dS^T = P^T (dP^T - D), packed to bf16 ----
+      const bool full = CAUSAL && j0 + BN - 1 <= qw0 && j0 + BN <= N;
+      const float bt0 = c2 * float(j0 + 4 * hi - i) - L;
+      u32x4 pf[PS];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * half + e;
+            const int jj = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+            float t = fmaf(s[kb][r], c1, bt0 + 32.0f * kb * c2);
+            if (!full) {
+              if (!CAUSAL && jj > i) t -= 2.0f * c2 * float(jj - i);
+              if (jj >= N || (CAUSAL && jj > i)) t = -__builtin_huge_valf();
+            }
+            const float pr = fast_exp2(t);
+            x[e] = pr * (dp[kb][r] - Dr);
+          }
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+          pf[2 * kb + half] = pk;
+        }
+      }
+      // ---- dQ^T += K^T dS^T ----
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int ps = 0; ps < PS; ++ps) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sKT + (32 * db + l32) * TPITCH + (16 * ps + 8 * hi) * 2);
+          acc[db] = mfma32(a, __builtin_bit_cast(bf16x8, pf[ps]), acc[db]);
+        }
+      }
+    }
+    if (tile > 0) store_tile(smem + (stage ^ 1) * STAGE);
+  }
+
+  if (i < N) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 st;
+        st[0] = pack_bf16x2(acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale);
+        st[1] = pack_bf16x2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale);
+        *reinterpret_cast<u32x2*>(dq + base + (long long)i * D + 32 * db + 8 * g + 4 * hi) = st;
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, hipStream_t stream) {
+  const long long rows = (long long)a.B * a.H * a.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(unsigned((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                     (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, dsum, lse2, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const float scale = float(1.0 / std::sqrt(double(D)));
+  const int nkb = (a.N + 127) / 128;
+  const long long tk = (long long)a.B * a.H * nkb;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(unsigned(tk)), dim3(256), 0, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
+                     nkb, int(tk), a.slopes, c1, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqb = (a.N + 127) / 128;
+  const long long tq = (long long)a.B * a.H * nqb;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(unsigned(tq)), dim3(256), 0, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dq, a.H, a.N, nqb, int(tq),
+                     a.slopes, c1, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, float* ws, float c1, hipStream_t stream) {
+  float* dsum = ws;
+  float* lse2 = ws + (long long)a.B * a.H * a.N;
+  if (a.d == 128)
+    return a.causal ? launch_bwd_cfg<128, true>(a, dsum, lse2, c1, stream)
+                    : launch_bwd_cfg<128, false>(a, dsum, lse2, c1, stream);
+  return a.causal ? launch_bwd_cfg<64, true>(a, dsum, lse2, c1, stream)
+                  : launch_bwd_cfg<64, false>(a, dsum, lse2, c1, stream);
+}
+
+}  // namespace alibi

@@ -10,6 +10,7 @@ namespace alibi {
 // exp(x) = exp2(x * log2(e)); the kernels carry scores in log2 units so that the
 // hardware exp2 (v_exp_f32) is the only transcendental.
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -36,6 +36,7 @@ struct GenParams {
   float softcap;    // z of z tanh(A / z)
   int delta;        // position of query row 0 minus position of key row 0
   float inv_sqrt_d;
+  float* lse;       // optional row log-sum-exp output (natural log)
 };
 
 template <typename T>
@@ -95,6 +96,7 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(
     m_run = m_new;
   }
   const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;  // a row that saw no key gives 0
+  if (gp.lse != nullptr && lane == 0) gp.lse[row] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : kNegInf;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int dd = lane + 64 * e;
@@ -154,6 +156,7 @@ hipError_t launch_fwd_generic(const FwdArgs& a, const FwdOptions& opt, bool f32,
   gp.softcap = opt.softcap;
   gp.delta = opt.q_offset - opt.k_offset;
   gp.inv_sqrt_d = float(1.0 / std::sqrt(double(a.d)));
+  gp.lse = opt.lse;
   if (f32)
     hipLaunchKernelGGL(fwd_generic_kernel<float>, dim3(grid), dim3(256), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,

@@ -175,6 +175,7 @@ struct FwdVariant {
   // of the key norms of each (b, h), or null.
   const float* knorm;
   int parts;
+  float* lse;  // optional (B, H, Nq) row log-sum-exp output, natural log
 };
 
 // A score whose exponent lies more than this many log2 units below the row's
@@ -469,6 +470,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // ---- epilogue: O / l -> bf16; a row that saw no key gives 0 ----
   const float lt = sum_xor32(l_run);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (var.lse != nullptr && i < Nq && hi == 0)
+    var.lse[(long long)bh * Nq + i] = lt > 0.0f ? (m_run + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
   if (i < Nq) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -520,6 +523,7 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hi
   var.cap_out = float(z * 1.4426950408889634);
   var.knorm = opt.knorm;
   var.parts = opt.knorm_parts;
+  var.lse = opt.lse;
   const int flags = opt.flags & 7;  // the mitigation bits; skipping is a run-time argument
   if (a.d == 128)
     return a.causal ? launch_var<128, true>(a, flags, c1, var, stream)

@@ -34,7 +34,28 @@ struct FwdOptions {
   // (launch_knorm_max), or null for no skipping
   const float* knorm = nullptr;
   int knorm_parts = 0;
+  // optional output: row log-sum-exp of the logits (natural log), (B, H, Nq)
+  float* lse = nullptr;
 };
+
+// One backward call (bf16 tensors (B, H, N, d), lse fp32 (B, H, N)).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N, d;
+  const float* slopes;
+  int causal;
+};
+
+// Backward, d in {64, 128}; ws holds 2 B H N floats (D and lse in log2 units).
+hipError_t launch_bwd(const BwdArgs& a, float* ws, float c1, hipStream_t stream);
 
 // Generic (VALU) forward, any d <= 256: fp32 (f32 = true) or bf16 data.
 hipError_t launch_fwd_generic(const FwdArgs& a, const FwdOptions& opt, bool f32, hipStream_t stream);

@@ -18,7 +18,8 @@ distances, soft cap 50; singly and all together), the symmetric non-causal
 bias, a chunked prefill (the last 512 query rows against the 4096-key
 cache through position offsets), and the exact underflow skipping (its rate
 counts the unskipped causal flops, so it is an effective rate, reported apart
-from the headline). Their flops are the algorithmic ones of each
+from the headline), and the backward pass (dq, dk, dv from the forward's
+log-sum-exp; 2.5x the forward's flops: five GEMMs of the causal triangle). Their flops are the algorithmic ones of each
 form: the causal triangle for the mitigations, N^2 without the mask, and the
 visible keys of the 512 rows for the prefill.
 
@@ -256,6 +257,13 @@ def next_forms(alibi, q, k, v, s, fw):
                              "ms": round(ms, 4),
                              "note": "exact skipping of all-underflow key tiles; key-norm pass included; "
                                      "flops are the unskipped causal count, so this is not the headline"}
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    alibi.attn_fwd_ex(q, k, v, s, True, out=out, lse=lse)
+    dout = torch.randn(q.shape, generator=torch.Generator(device=q.device).manual_seed(7), device=q.device,
+                       dtype=torch.float32).to(torch.bfloat16)
+    ms = time_launches(lambda: alibi.attn_bwd(q, k, v, out, dout, lse, s, True), warmup=5, reps=10)
+    res["backward"] = {"value": round(2.5 * causal_flops / ms / 1e9, 1), "unit": "TFLOP/s", "ms": round(ms, 4),
+                       "note": "dq, dk, dv; flops = 5 causal GEMMs (S, dP, dV, dK, dQ) = 2.5x the forward's"}
     nq = 512
     qc = q[:, :, N - nq:].contiguous()
     oc = torch.empty_like(qc)

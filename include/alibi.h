@@ -154,6 +154,9 @@ typedef struct alibi_fwd_opts {
   float softcap;     /* z > 0, finite (e.g. 50); used with ALIBI_SOFTCAP */
   int q_offset;      /* position of query row 0, 0 .. 2^24 */
   int k_offset;      /* position of key row 0, 0 .. 2^24 */
+  float* lse;        /* optional device fp32 (B, H, Nq) output: each row's natural-log
+                        log-sum-exp of its logits (-inf for a row that sees no key),
+                        what alibi_attn_bwd needs; NULL = not written; 4-byte aligned */
 } alibi_fwd_opts;
 
 /*
@@ -183,6 +186,25 @@ int alibi_attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
 int alibi_attn_fwd_ex_f32(const float* q, const float* k, const float* v, float* out,
                           int B, int H, int Nq, int Nk, int d, const float* slopes, int causal,
                           const alibi_fwd_opts* opts, hipStream_t stream);
+
+/*
+ * Backward pass: gradients of the plain ALiBi forward (no mitigation, no
+ * offsets) with respect to q, k and v; the bias is a constant (the slopes are
+ * fixed, abhik.ai "Different heads, different distance penalties").
+ * With P = exp(logits - lse) recomputed per tile from the forward's lse:
+ *   dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dO * O)),
+ *   dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
+ * q, k, v, out (the forward's output), dout, dq, dk, dv: device bf16
+ * (B, H, N, d) contiguous, 16-byte aligned; lse: device fp32 (B, H, N) from
+ * alibi_attn_fwd_ex's opts->lse; slopes: device, H fp32; causal as in the
+ * forward. d must be 64 or 128 (ALIBI_ENOTSUP otherwise). Uses a
+ * library-owned per-device workspace of 2 B H N floats: order calls on one
+ * device on one stream. dq, dk, dv may not alias the inputs.
+ */
+int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, const float* slopes, int causal,
+                   hipStream_t stream);
 
 /*
  * Slope recipes from target blindness distances (host only). A head whose bias
