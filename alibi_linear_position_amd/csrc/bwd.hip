@@ -15,14 +15,14 @@
 // * bwd_dkdv_kernel: one workgroup per 128 keys of one (b, h); each of its 4
 //   waves owns 32 keys and keeps their K and V rows as MFMA B operands in
 //   registers, and the dK^T, dV^T accumulators. Query tiles of 32 rows stream
-//   through LDS (double-buffered): Q and dO row-major for S = Q K^T and
-//   dP = dO V^T (rows = queries, lane = key), and transposed with the same key
-//   permutation as the forward's V^T for dV^T += dO^T P and dK^T += Q^T dS, so
-//   P and dS go from registers to the next MFMA as B operands.
+//   through LDS (double-buffered), row-major: read straight for S = Q K^T and
+//   dP = dO V^T (rows = queries, lane = key), and read transposed
+//   (ds_read_b64_tr_b16) for dV^T += dO^T P and dK^T += Q^T dS, so P and dS go
+//   from registers to the next MFMA as B operands.
 // * bwd_dq_kernel: one workgroup per 128 queries, the forward's layout:
 //   S^T = K Q^T and dP^T = V dO^T (lane = query, so lse and D are one value
-//   per lane), dS^T packed to bf16 and dQ^T += K^T dS^T; K row-major, K^T and
-//   V row-major staged per 64-key tile.
+//   per lane), dS^T packed to bf16 and dQ^T += K^T dS^T, with K^T read
+//   transposed from the row-major K tile; K and V staged per 64-key tile.
 // Scores are in log2 units (c1 = log2(e) / sqrt(d), c2 = m log2(e)); masked and
 // out-of-range entries get P = 0.
 #include "device_common.h"
@@ -37,10 +37,6 @@ namespace {
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-
-// Position of index x (0..15) inside a 16-wide MFMA k-step whose B operand comes
-// from an accumulator: swaps 4-7 with 8-11.
-__device__ __forceinline__ int perm16(int x) { return ((x & 4) << 1) | ((x & 8) >> 1) | (x & 3); }
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -88,10 +84,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int NT = 256, BK = 128, BQ = 32;
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int RPITCH = D * 2 + 16;  // row-major Q / dO rows, bytes
-  constexpr int TPITCH = BQ * 2 + 16; // transposed [d][query], bytes
   constexpr int RBYTES = BQ * RPITCH;
-  constexpr int TBYTES = D * TPITCH;
-  constexpr int STAGE = 2 * RBYTES + 2 * TBYTES + 2 * BQ * 4;
+  constexpr int STAGE = 2 * RBYTES + 2 * BQ * 4;
   constexpr int LOADS = BQ * CPR / NT;  // 16-byte chunks of Q (and of dO) per thread
   static_assert(LOADS * NT == BQ * CPR, "tile must split evenly");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
@@ -164,23 +158,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   auto store_tile = [&](unsigned char* st) {
     unsigned char* sQ = st;
     unsigned char* sO = st + RBYTES;
-    unsigned char* sQT = st + 2 * RBYTES;
-    unsigned char* sOT = sQT + TBYTES;
-    float* sL = reinterpret_cast<float*>(sOT + TBYTES);
+    float* sL = reinterpret_cast<float*>(st + 2 * RBYTES);
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
       const int c = tid + NT * r, row = c / CPR, col = c % CPR;
       *reinterpret_cast<u32x4*>(sQ + row * RPITCH + col * 16) = rq[r];
       *reinterpret_cast<u32x4*>(sO + row * RPITCH + col * 16) = rdo[r];
-      const int pos = (row & ~15) | perm16(row & 15);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d0 = col * 8 + 2 * e;
-        *reinterpret_cast<uint16_t*>(sQT + d0 * TPITCH + pos * 2) = uint16_t(rq[r][e] & 0xffffu);
-        *reinterpret_cast<uint16_t*>(sQT + (d0 + 1) * TPITCH + pos * 2) = uint16_t(rq[r][e] >> 16);
-        *reinterpret_cast<uint16_t*>(sOT + d0 * TPITCH + pos * 2) = uint16_t(rdo[r][e] & 0xffffu);
-        *reinterpret_cast<uint16_t*>(sOT + (d0 + 1) * TPITCH + pos * 2) = uint16_t(rdo[r][e] >> 16);
-      }
     }
     if (tid < BQ) {
       sL[tid] = rl;
@@ -199,9 +182,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const unsigned char* st = smem + stage * STAGE;
     const unsigned char* sQ = st;
     const unsigned char* sO = st + RBYTES;
-    const unsigned char* sQT = st + 2 * RBYTES;
-    const unsigned char* sOT = sQT + TBYTES;
-    const float* sL = reinterpret_cast<const float*>(sOT + TBYTES);
+    const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
     const int q0 = qt * BQ;
     const bool active = !CAUSAL || q0 + BQ - 1 >= kw0;
     if (active) {
@@ -244,12 +225,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       // ---- dV^T += dO^T P, dK^T += Q^T dS ----
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const unsigned char* ro = sOT + (32 * db + l32) * TPITCH + 8 * hi * 2;
-        const unsigned char* rq2 = sQT + (32 * db + l32) * TPITCH + 8 * hi * 2;
-        dva[db] = mfma32(*reinterpret_cast<const bf16x8*>(ro), __builtin_bit_cast(bf16x8, pb0), dva[db]);
-        dva[db] = mfma32(*reinterpret_cast<const bf16x8*>(ro + 32), __builtin_bit_cast(bf16x8, pb1), dva[db]);
-        dka[db] = mfma32(*reinterpret_cast<const bf16x8*>(rq2), __builtin_bit_cast(bf16x8, sb0), dka[db]);
-        dka[db] = mfma32(*reinterpret_cast<const bf16x8*>(rq2 + 32), __builtin_bit_cast(bf16x8, sb1), dka[db]);
+        dva[db] = mfma32(read_tr(sO, RPITCH, 0, 32 * db, lane), __builtin_bit_cast(bf16x8, pb0), dva[db]);
+        dva[db] = mfma32(read_tr(sO, RPITCH, 16, 32 * db, lane), __builtin_bit_cast(bf16x8, pb1), dva[db]);
+        dka[db] = mfma32(read_tr(sQ, RPITCH, 0, 32 * db, lane), __builtin_bit_cast(bf16x8, sb0), dka[db]);
+        dka[db] = mfma32(read_tr(sQ, RPITCH, 16, 32 * db, lane), __builtin_bit_cast(bf16x8, sb1), dka[db]);
       }
     }
     if (qt + 1 < nqt) store_tile(smem + (stage ^ 1) * STAGE);
@@ -284,9 +263,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   constexpr int NT = 256, BM = 128, BN = 64;
   constexpr int KS = D / 16, KB = BN / 32, DB = D / 32, PS = BN / 16, CPR = D / 8;
   constexpr int KPITCH = D * 2 + 16;   // K and V rows, bytes
-  constexpr int TPITCH = BN * 2 + 16;  // K^T [d][key], bytes
   constexpr int KBYTES = BN * KPITCH;
-  constexpr int STAGE = 2 * KBYTES + D * TPITCH;
+  constexpr int STAGE = 2 * KBYTES;
   constexpr int LOADS = BN * CPR / NT;
   static_assert(LOADS * NT == BN * CPR, "tile must split evenly");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
@@ -331,36 +309,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
 
-  // K chunks go one key per lane (so the transposed writes of a wave cover
-  // whole 16-key groups), V chunks row-major.
   u32x4 rk[LOADS], rv[LOADS];
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
-      const int key = tid % BN, col = tid / BN + (NT / BN) * r;
+      const int c = tid + NT * r, row = c / CPR, col = c % CPR;
       rk[r] = u32x4{0u, 0u, 0u, 0u};
-      if (j0 + key < N) rk[r] = load16(k + base + (long long)(j0 + key) * D + col * 8);
-      const int c = tid + NT * r, row = c / CPR, vc = c % CPR;
       rv[r] = u32x4{0u, 0u, 0u, 0u};
-      if (j0 + row < N) rv[r] = load16(v + base + (long long)(j0 + row) * D + vc * 8);
+      if (j0 + row < N) {
+        rk[r] = load16(k + base + (long long)(j0 + row) * D + col * 8);
+        rv[r] = load16(v + base + (long long)(j0 + row) * D + col * 8);
+      }
     }
   };
   auto store_tile = [&](unsigned char* st) {
-    unsigned char* sK = st;
-    unsigned char* sV = st + KBYTES;
-    unsigned char* sKT = st + 2 * KBYTES;
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
-      const int key = tid % BN, col = tid / BN + (NT / BN) * r;
-      *reinterpret_cast<u32x4*>(sK + key * KPITCH + col * 16) = rk[r];
-      const int pos = (key & ~15) | perm16(key & 15);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint16_t*>(sKT + (col * 8 + 2 * e) * TPITCH + pos * 2) = uint16_t(rk[r][e] & 0xffffu);
-        *reinterpret_cast<uint16_t*>(sKT + (col * 8 + 2 * e + 1) * TPITCH + pos * 2) = uint16_t(rk[r][e] >> 16);
-      }
-      const int c = tid + NT * r, row = c / CPR, vc = c % CPR;
-      *reinterpret_cast<u32x4*>(sV + row * KPITCH + vc * 16) = rv[r];
+      const int c = tid + NT * r, row = c / CPR, col = c % CPR;
+      *reinterpret_cast<u32x4*>(st + row * KPITCH + col * 16) = rk[r];
+      *reinterpret_cast<u32x4*>(st + KBYTES + row * KPITCH + col * 16) = rv[r];
     }
   };
 
@@ -376,7 +343,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const unsigned char* st = smem + stage * STAGE;
     const unsigned char* sK = st;
     const unsigned char* sV = st + KBYTES;
-    const unsigned char* sKT = st + 2 * KBYTES;
     const bool active = qw0 < N && (!CAUSAL || j0 <= qw_last);
     if (active) {
       // ---- S^T = K Q^T, dP^T = V dO^T (lane = query) ----
@@ -422,10 +388,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
-        for (int ps = 0; ps < PS; ++ps) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sKT + (32 * db + l32) * TPITCH + (16 * ps + 8 * hi) * 2);
-          acc[db] = mfma32(a, __builtin_bit_cast(bf16x8, pf[ps]), acc[db]);
-        }
+        for (int ps = 0; ps < PS; ++ps)
+          acc[db] = mfma32(read_tr(sK, KPITCH, 16 * ps, 32 * db, lane), __builtin_bit_cast(bf16x8, pf[ps]), acc[db]);
       }
     }
     if (tile > 0) store_tile(smem + (stage ^ 1) * STAGE);
