@@ -183,7 +183,9 @@ struct FwdVariant {
 // subnormal is 2^-133); the skipping bound uses 140 plus the lazy-rescale lag.
 constexpr float kDeadLog2 = 140.0f + kLazy;
 
-template <int D, int NW, bool CAUSAL, int VAR>
+// EXT = false compiles the plain call (alibi_attn_fwd: no offsets, no
+// skipping, no log-sum-exp output) without those paths.
+template <int D, int NW, bool CAUSAL, int VAR, bool EXT>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, int H, int Nq, int Nk, int nqb, int total,
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   const int i = qw0 + l32;                             // this lane's query row
   // Query row i sits at key-index position pi: key j is visible to it when
   // j <= pi (causal) and lies at distance pi - j.
-  const int delta = var.delta;
+  const int delta = EXT ? var.delta : 0;
   const int pi = i + delta;
 
   // C operand of the first Q K^T k-step: seeds register r of a 32-key block
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // of its waves still needs, and a wave skips its own dead tiles before that.
   __shared__ int s_dead[NW];
   int t_dead_wave = -1, t_dead = -1;
-  if (CAUSAL && VAR == 0 && var.knorm != nullptr && c2 > 0.0f) {
+  if (EXT && CAUSAL && VAR == 0 && var.knorm != nullptr && c2 > 0.0f) {
     float kmax = 0.0f;
     for (int p = 0; p < var.parts; ++p) kmax = fmaxf(kmax, var.knorm[(long long)bh * var.parts + p]);
     float qn2 = 0.0f;
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // ---- epilogue: O / l -> bf16; a row that saw no key gives 0 ----
   const float lt = sum_xor32(l_run);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (var.lse != nullptr && i < Nq && hi == 0)
+  if (EXT && var.lse != nullptr && i < Nq && hi == 0)
     var.lse[(long long)bh * Nq + i] = lt > 0.0f ? (m_run + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
   if (i < Nq) {
 #pragma unroll
@@ -486,29 +488,31 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   }
 }
 
-template <int D, int NW, bool CAUSAL, int VAR>
+template <int D, int NW, bool CAUSAL, int VAR, bool EXT>
 hipError_t launch_cfg(const FwdArgs& a, float c1, const FwdVariant& var, hipStream_t stream) {
   constexpr int BM = NW * 32;
   const int nqb = (a.Nq + BM - 1) / BM;
   const long long total = (long long)a.B * a.H * nqb;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, CAUSAL, VAR>), dim3(unsigned(total)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, CAUSAL, VAR, EXT>), dim3(unsigned(total)), dim3(NW * 64), 0,
                      stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.out, a.H, a.Nq, a.Nk, nqb, int(total), a.slopes, c1, var);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_var(const FwdArgs& a, int flags, float c1, const FwdVariant& var, hipStream_t s) {
+hipError_t launch_var(const FwdArgs& a, int flags, bool ext, float c1, const FwdVariant& var, hipStream_t s) {
   switch (flags) {
-    case 0: return fwd_waves() == 8 ? launch_cfg<D, 8, CAUSAL, 0>(a, c1, var, s)
-                                    : launch_cfg<D, 4, CAUSAL, 0>(a, c1, var, s);
-    case 1: return launch_cfg<D, 4, CAUSAL, 1>(a, c1, var, s);
-    case 2: return launch_cfg<D, 4, CAUSAL, 2>(a, c1, var, s);
-    case 3: return launch_cfg<D, 4, CAUSAL, 3>(a, c1, var, s);
-    case 4: return launch_cfg<D, 4, CAUSAL, 4>(a, c1, var, s);
-    case 5: return launch_cfg<D, 4, CAUSAL, 5>(a, c1, var, s);
-    case 6: return launch_cfg<D, 4, CAUSAL, 6>(a, c1, var, s);
-    default: return launch_cfg<D, 4, CAUSAL, 7>(a, c1, var, s);
+    case 0:
+      if (ext) return launch_cfg<D, 4, CAUSAL, 0, true>(a, c1, var, s);
+      return fwd_waves() == 8 ? launch_cfg<D, 8, CAUSAL, 0, false>(a, c1, var, s)
+                              : launch_cfg<D, 4, CAUSAL, 0, false>(a, c1, var, s);
+    case 1: return launch_cfg<D, 4, CAUSAL, 1, true>(a, c1, var, s);
+    case 2: return launch_cfg<D, 4, CAUSAL, 2, true>(a, c1, var, s);
+    case 3: return launch_cfg<D, 4, CAUSAL, 3, true>(a, c1, var, s);
+    case 4: return launch_cfg<D, 4, CAUSAL, 4, true>(a, c1, var, s);
+    case 5: return launch_cfg<D, 4, CAUSAL, 5, true>(a, c1, var, s);
+    case 6: return launch_cfg<D, 4, CAUSAL, 6, true>(a, c1, var, s);
+    default: return launch_cfg<D, 4, CAUSAL, 7, true>(a, c1, var, s);
   }
 }
 
@@ -525,11 +529,12 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hi
   var.parts = opt.knorm_parts;
   var.lse = opt.lse;
   const int flags = opt.flags & 7;  // the mitigation bits; skipping is a run-time argument
+  const bool ext = var.delta != 0 || var.knorm != nullptr || var.lse != nullptr;
   if (a.d == 128)
-    return a.causal ? launch_var<128, true>(a, flags, c1, var, stream)
-                    : launch_var<128, false>(a, flags, c1, var, stream);
-  return a.causal ? launch_var<64, true>(a, flags, c1, var, stream)
-                  : launch_var<64, false>(a, flags, c1, var, stream);
+    return a.causal ? launch_var<128, true>(a, flags, ext, c1, var, stream)
+                    : launch_var<128, false>(a, flags, ext, c1, var, stream);
+  return a.causal ? launch_var<64, true>(a, flags, ext, c1, var, stream)
+                  : launch_var<64, false>(a, flags, ext, c1, var, stream);
 }
 
 }  // namespace alibi

@@ -28,9 +28,10 @@ bounded sample (whole heads of the same forward, whole (b, h) pairs of the
 same decode), scaled to the same units.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --only fwd|decode|copy [--steps K] [--warmup W]
+    python bench.py --only fwd|decode|copy|bwd [--steps K] [--warmup W]
 
-`--only` runs a single kernel (or, for `copy`, a plain device-to-device copy of
+`--only` runs a single kernel (`bwd`: the three backward kernels; `copy`: a
+plain device-to-device copy of
 a 1 GiB bf16 tensor) so that hardware-counter runs see one kernel; it prints a
 short JSON line and no CPU baseline. The copy calibrates the HBM byte counters.
 """
@@ -125,7 +126,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None)
+    ap.add_argument("--only", choices=["fwd", "decode", "copy", "bwd"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -202,7 +203,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes("fwd_mfma_B8_H16_N4096_d128.md", ["fwd_mfma.hip", "device_common.h"]),
-                     "kernel": f"fwd_mfma_kernel<128,{os.environ.get('ALIBI_FWD_NW', '4')},true>", "ms_per_launch": round(t_fwd * 1e3, 4),
+                     "kernel": f"fwd_mfma_kernel<128,{os.environ.get('ALIBI_FWD_NW', '4')},true,0,false>", "ms_per_launch": round(t_fwd * 1e3, 4),
                      "per_launch": f"{flops:.4e} flop"},
         "decode": {"value": round(gbs, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
@@ -291,6 +292,14 @@ def run_only(args, alibi, W, fw, dw, dev):
         s = alibi.slopes(dw.H).to(dev)
         fn = lambda: alibi.attn_decode(qd, kc, vc, s, out=od)
         work, unit = decode_bytes(dw.B, dw.H, dw.L, dw.d), "B"
+    elif args.only == "bwd":
+        q, k, v = (x.to(dev) for x in W.gaussian_qkv_bf16(fw.shape, seed=fw.seed))
+        s = alibi.slopes(fw.H).to(dev)
+        out, lse = alibi.attn_fwd_train(q, k, v, s, True)
+        dout = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
+                           dtype=torch.float32).to(torch.bfloat16)
+        fn = lambda: alibi.attn_bwd(q, k, v, out, dout, lse, s, True)
+        work, unit = 2.5 * fwd_flops(fw.B, fw.H, fw.N, fw.d), "flop"
     else:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
