@@ -68,6 +68,8 @@ int fwd_waves() {
   return nw;
 }
 constexpr float kLazy = 8.0f;
+// Largest partial row sum (32 keys of one lane) accepted without a fresh bound.
+constexpr float kOptLimit = 65536.0f;
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family parts:
 // 32-bit data format, byte-granular range check against the record count.
 constexpr int kBufferFlags = 0x00020000;
@@ -380,67 +382,90 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const float bt0 = c2 * float(j0 + 4 * hi - pi);
     const float bt1 = bt0 + 32.0f * c2;
     const float dpos = float(pi - j0 - 4 * hi);  // distance of register 0 of key block 0
-    float mcand;
-    if (VAR == 0 && !MASKED) {
-      // every key is visible: max16 of s bounds the row maximum
-      mcand = max_xor32(fmaxf(fmaf(max16(s[0]), c1, bt0), fmaf(max16(s[1]), c1, bt1)));
-    } else {
-      // masked keys become -inf in s itself, so the exponent code is shared
-      float tmax = kNegInf;
+    // p = exp2(s sc + bias_kb) packed to bf16 (the P^T B operand), with the
+    // row sum taken from the same bf16 values.
+    u32x4 pf[PS];
+    const float sc = VAR == 0 ? c1 : 1.0f;
+    auto exp_block = [&](float b0, float b1) {
+      float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-          const int j = j0 + 4 * hi + off;
-          float x;
-          if constexpr (VAR == 0) {
-            x = s[kb][r];
-            if (!CAUSAL && j > pi) x -= 2.0f * c21 * float(j - pi);  // symmetric bias -m |i - j|
-          } else {
-            x = variant_t(s[kb][r], dpos - float(off));
+        for (int half = 0; half < 2; ++half) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r0 = 8 * half + 2 * e;
+            const float bb = kb ? b1 : b0;
+            pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], sc, bb)), fast_exp2(fmaf(s[kb][r0 + 1], sc, bb)));
+            lpart[e] = bdot2(pk[e], lpart[e]);
           }
-          if (MASKED) x = (j < Nk && (!CAUSAL || j <= pi)) ? x : kNegInf;
-          s[kb][r] = x;
-          tmax = fmaxf(tmax, VAR == 0 ? fmaf(x, c1, kb ? bt1 : bt0) : x);
+          pf[2 * kb + half] = pk;
         }
       }
-      mcand = max_xor32(tmax);
-    }
+      return (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+    };
     // Lazy rescale: the running maximum moves only when a row's candidate
-    // exceeds it by more than 2^kLazy, so p stays below 2^kLazy.
-    const bool need = mcand > m_run + kLazy;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mcand : m_run;
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
-      l_run *= alpha;
+    // exceeds it by more than 2^kLazy.
+    auto rescale = [&](float mcand) {
+      const bool need = mcand > m_run + kLazy;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mcand : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      m_run = m_new;
-    }
-    // m_run is finite after the first visible key; a row with none yet
-    // (every key masked) keeps -inf and takes 0 here
-    const float m_use = MASKED && m_run == kNegInf ? 0.0f : m_run;
-    u32x4 pf[PS];
-    float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
-    const float sc = VAR == 0 ? c1 : 1.0f;
-    const float b0 = (VAR == 0 ? bt0 : 0.0f) - m_use, b1 = (VAR == 0 ? bt1 : 0.0f) - m_use;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r0 = 8 * half + 2 * e;
-          const float bb = kb ? b1 : b0;
-          pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], sc, bb)), fast_exp2(fmaf(s[kb][r0 + 1], sc, bb)));
-          lpart[e] = bdot2(pk[e], lpart[e]);
-        }
-        pf[2 * kb + half] = pk;
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        m_run = m_new;
       }
+    };
+    float lsum;
+    if (VAR == 0 && !MASKED) {
+      // Every key is visible and tiles go from the diagonal outwards, so the
+      // running maximum is almost always already above this tile's scores:
+      // exponentiate against it directly. A lane whose partial row sum leaves
+      // (0, kOptLimit] (a score above the maximum by ~2^11, an overflow, or a
+      // row without a finite maximum yet) sends the wave through the bound and
+      // the rescale, and the tile is redone.
+      lsum = exp_block(bt0 - m_run, bt1 - m_run);
+      if (__builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit))) {
+        rescale(max_xor32(fmaxf(fmaf(max16(s[0]), c1, bt0), fmaf(max16(s[1]), c1, bt1))));
+        lsum = exp_block(bt0 - m_run, bt1 - m_run);
+      }
+    } else {
+      float mcand;
+      if (VAR == 0 && !MASKED) {
+        // every key is visible: max16 of s bounds the row maximum
+        mcand = max_xor32(fmaxf(fmaf(max16(s[0]), c1, bt0), fmaf(max16(s[1]), c1, bt1)));
+      } else {
+        // masked keys become -inf in s itself, so the exponent code is shared
+        float tmax = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+            const int j = j0 + 4 * hi + off;
+            float x;
+            if constexpr (VAR == 0) {
+              x = s[kb][r];
+              if (!CAUSAL && j > pi) x -= 2.0f * c21 * float(j - pi);  // symmetric bias -m |i - j|
+            } else {
+              x = variant_t(s[kb][r], dpos - float(off));
+            }
+            if (MASKED) x = (j < Nk && (!CAUSAL || j <= pi)) ? x : kNegInf;
+            s[kb][r] = x;
+            tmax = fmaxf(tmax, VAR == 0 ? fmaf(x, c1, kb ? bt1 : bt0) : x);
+          }
+        }
+        mcand = max_xor32(tmax);
+      }
+      rescale(mcand);
+      // m_run is finite after the first visible key; a row with none yet
+      // (every key masked) keeps -inf and takes 0 here
+      const float m_use = MASKED && m_run == kNegInf ? 0.0f : m_run;
+      lsum = exp_block((VAR == 0 ? bt0 : 0.0f) - m_use, (VAR == 0 ? bt1 : 0.0f) - m_use);
     }
-    l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+    l_run += lsum;
 
     // ---- O^T += V^T P^T, with the next tile's LDS stores in the same region ----
 #pragma unroll
