@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
 // ---------------------------------------------------------------- dQ --------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dq, int H, int N, int nqb, int total, const float* __restrict__ slopes,
@@ -345,24 +345,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const unsigned char* sV = st + KBYTES;
     const bool active = qw0 < N && (!CAUSAL || j0 <= qw_last);
     if (active) {
-      // ---- S^T = K Q^T, dP^T = V dO^T (lane = query) ----
-      f32x16 s[KB], dp[KB];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
-          s[kb] = mfma32(a, qf[ks], ks == 0 ? cinit : s[kb]);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(sV + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
-          dp[kb] = mfma32(b, of[ks], ks == 0 ? f32x16{} : dp[kb]);
-        }
-      }
-      // ---- P^T = exp2(t - lse2), dS^T = P^T (dP^T - D), packed to bf16 ----
+      // ---- per 32-key block: S^T = K Q^T, dP^T = V dO^T (lane = query), then
+      // P^T = exp2(t - lse2) and dS^T = P^T (dP^T - D) packed to bf16 ----
       const bool full = CAUSAL && j0 + BN - 1 <= qw0 && j0 + BN <= N;
       const float bt0 = c2 * float(j0 + 4 * hi - i) - L;
       u32x4 pf[PS];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
+        f32x16 s = cinit, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
+          s = mfma32(a, qf[ks], s);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(sV + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
+          dp = mfma32(b, of[ks], dp);
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           float x[8];
@@ -370,13 +367,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * half + e;
             const int jj = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-            float t = fmaf(s[kb][r], c1, bt0 + 32.0f * kb * c2);
+            float t = fmaf(s[r], c1, bt0 + 32.0f * kb * c2);
             if (!full) {
               if (!CAUSAL && jj > i) t -= 2.0f * c2 * float(jj - i);
               if (jj >= N || (CAUSAL && jj > i)) t = -__builtin_huge_valf();
             }
-            const float pr = fast_exp2(t);
-            x[e] = pr * (dp[kb][r] - Dr);
+            x[e] = fast_exp2(t) * (dp[r] - Dr);
           }
           u32x4 pk;
 #pragma unroll

@@ -206,3 +206,17 @@ def test_decode_full_config_sampled_heads(alibi):
         check_bf16(out[b:b + 1, h:h + 1], ref, f"{wl.name} b{b} h{h}")
     del kc, vc
     torch.cuda.empty_cache()
+
+
+def test_fwd_far_key_dominates_rows(alibi):
+    # A key far behind the diagonal scores far above every nearer key (q_i . k_j
+    # large), so an off-diagonal tile must raise the running maximum well past
+    # what the diagonal set: the rare rescale-and-redo path of the kernel.
+    B, H, N, d = 1, 2, 1500, 128
+    q, k, v = W.gaussian_qkv_f32((B, H, N, d), seed=41)
+    q[:, :, 1200:1300] = k[:, :, 10:11] * 3.0      # rows 1200..1299 align with key 10
+    qb, kb, vb = (W.to_bf16_tensor(x) for x in (q, k, v))
+    s = np.array([0.01, 0.001], dtype=np.float32)
+    out = alibi.attn_fwd(dev(qb), dev(kb), dev(vb), torch.from_numpy(s), causal=True)
+    ref = oracle.attn_ref(qb, kb, vb, s, causal=True)
+    check_bf16(out, ref, "far key dominates")
