@@ -12,9 +12,9 @@
 // Three kernels:
 // * bwd_prep_kernel: D_i and the log-sum-exp in log2 units, one lane group
 //   per row.
-// * bwd_dkdv_kernel: one workgroup per 128 keys of one (b, h); each of its 4
-//   waves owns 32 keys and keeps their K and V rows as MFMA B operands in
-//   registers, and the dK^T, dV^T accumulators. Query tiles of 32 rows stream
+// * bwd_dkdv_kernel: one workgroup per 128 keys of one (b, h), eight waves:
+//   four own dV and four own dK of 32 keys each, keeping their keys' K (and V)
+//   rows as MFMA B operands in registers. Query tiles of 32 rows stream
 //   through LDS (double-buffered), row-major: read straight for S = Q K^T and
 //   dP = dO V^T (rows = queries, lane = key), and read transposed
 //   (ds_read_b64_tr_b16) for dV^T += dO^T P and dK^T += Q^T dS, so P and dS go
@@ -75,23 +75,29 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------- dK, dV ----
+// Eight waves: waves 0-3 own dV and waves 4-7 own dK of the same 4 x 32 keys
+// (waves w and w + 4 share a SIMD). A dV wave computes S and P and
+// accumulates dV^T += dO^T P; a dK wave computes S, dP and dS and accumulates
+// dK^T += Q^T dS. S is computed twice, but each wave holds one accumulator set,
+// so two waves fit on every SIMD.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int H, int N, int nkb, int total,
     const float* __restrict__ slopes, float c1, float scale) {
-  constexpr int NT = 256, BK = 128, BQ = 32;
+  constexpr int NT = 512, BK = 128, BQ = 32;
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int RPITCH = D * 2 + 16;  // row-major Q / dO rows, bytes
   constexpr int RBYTES = BQ * RPITCH;
   constexpr int STAGE = 2 * RBYTES + 2 * BQ * 4;
-  constexpr int LOADS = BQ * CPR / NT;  // 16-byte chunks of Q (and of dO) per thread
-  static_assert(LOADS * NT == BQ * CPR, "tile must split evenly");
+  constexpr int CHUNKS = BQ * CPR;    // 16-byte chunks of Q (and of dO) per tile
+  static_assert(CHUNKS <= NT, "one chunk per thread at most");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave >> 2;  // 0: dV, 1: dK
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int w = blockIdx.x;
   const int lw = (total & 7) == 0 ? (w & 7) * (total >> 3) + (w >> 3) : w;
@@ -103,51 +109,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const long long base = (long long)bh * N * D;
   const long long rbase = (long long)bh * N;
   const int k0 = kblk * BK;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + (wave & 3) * 32;
   const int j = kw0 + l32;  // this lane's key
 
-  // K and V rows of this lane's key as B operands (k index = d).
-  bf16x8 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (j < N) {
-      a = load16(k + base + (long long)j * D + 16 * ks + 8 * hi);
-      b = load16(v + base + (long long)j * D + 16 * ks + 8 * hi);
-    }
-    kf[ks] = __builtin_bit_cast(bf16x8, a);
-    vf[ks] = __builtin_bit_cast(bf16x8, b);
-  }
   // S rows are queries 8 (r / 4) + 4 hi + r % 4 of the tile; seeding register r
   // with -c2 / c1 (8 (r / 4) + r % 4) leaves one fma for the bias.
   f32x16 cinit;
 #pragma unroll
   for (int r = 0; r < 16; ++r) cinit[r] = -c21 * float(8 * (r >> 2) + (r & 3));
 
-  f32x16 dka[DB], dva[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dka[db] = f32x16{};
-    dva[db] = f32x16{};
-  }
-
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? k0 / BQ : 0;
 
-  // staging registers of one query tile
-  u32x4 rq[LOADS], rdo[LOADS];
+  // staging registers of one query tile (one chunk of Q and of dO per thread)
+  u32x4 rq = {0u, 0u, 0u, 0u}, rdo = {0u, 0u, 0u, 0u};
   float rl = 0.0f, rd = 0.0f;
   auto load_tile = [&](int qt) {
     const int q0 = qt * BQ;
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int c = tid + NT * r, row = c / CPR, col = c % CPR;
-      rq[r] = u32x4{0u, 0u, 0u, 0u};
-      rdo[r] = u32x4{0u, 0u, 0u, 0u};
-      if (q0 + row < N) {
-        rq[r] = load16(q + base + (long long)(q0 + row) * D + col * 8);
-        rdo[r] = load16(dout + base + (long long)(q0 + row) * D + col * 8);
-      }
+    const int row = tid / CPR, col = tid % CPR;
+    rq = u32x4{0u, 0u, 0u, 0u};
+    rdo = u32x4{0u, 0u, 0u, 0u};
+    if (tid < CHUNKS && q0 + row < N) {
+      rq = load16(q + base + (long long)(q0 + row) * D + col * 8);
+      rdo = load16(dout + base + (long long)(q0 + row) * D + col * 8);
     }
     if (tid < BQ) {
       const bool ok = q0 + tid < N;
@@ -156,18 +140,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
   };
   auto store_tile = [&](unsigned char* st) {
-    unsigned char* sQ = st;
-    unsigned char* sO = st + RBYTES;
-    float* sL = reinterpret_cast<float*>(st + 2 * RBYTES);
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int c = tid + NT * r, row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(sQ + row * RPITCH + col * 16) = rq[r];
-      *reinterpret_cast<u32x4*>(sO + row * RPITCH + col * 16) = rdo[r];
+    const int row = tid / CPR, col = tid % CPR;
+    if (tid < CHUNKS) {
+      *reinterpret_cast<u32x4*>(st + row * RPITCH + col * 16) = rq;
+      *reinterpret_cast<u32x4*>(st + RBYTES + row * RPITCH + col * 16) = rdo;
     }
     if (tid < BQ) {
+      float* sL = reinterpret_cast<float*>(st + 2 * RBYTES);
       sL[tid] = rl;
       sL[BQ + tid] = rd;
+    }
+  };
+  auto load_frags = [&](const uint16_t* src, bf16x8 (&f)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (j < N) a = load16(src + base + (long long)j * D + 16 * ks + 8 * hi);
+      f[ks] = __builtin_bit_cast(bf16x8, a);
+    }
+  };
+  // S = Q K^T (rows = queries, lane = key) and P = exp2(t - lse2) of one tile
+  auto scores = [&](const unsigned char* sQ, const bf16x8 (&kf)[KS]) {
+    f32x16 s = cinit;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + l32 * RPITCH + (16 * ks + 8 * hi) * 2);
+      s = mfma32(a, kf[ks], s);
+    }
+    return s;
+  };
+  auto probs = [&](f32x16& s, const float* sL, int q0) {
+    const float bj = c2 * float(j - q0 - 4 * hi);  // t = s c1 + bj on the causal side
+    const bool full = CAUSAL && q0 >= kw0 + 31;    // every query of the tile sees every key of the wave
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 L = *reinterpret_cast<const f32x4*>(sL + 8 * g + 4 * hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        const int i = q0 + 8 * g + 4 * hi + e;
+        float t = fmaf(s[r], c1, bj);
+        if (!full) {
+          if (!CAUSAL && j > i) t -= 2.0f * c2 * float(j - i);  // symmetric bias -m |i - j|
+          if (CAUSAL && j > i) t = -__builtin_huge_valf();
+        }
+        s[r] = fast_exp2(t - L[e]);
+      }
     }
   };
 
@@ -175,79 +193,82 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     load_tile(qt0);
     store_tile(smem);
   }
-  int stage = 0;
-  for (int qt = qt0; qt < nqt; ++qt, stage ^= 1) {
-    __syncthreads();
-    if (qt + 1 < nqt) load_tile(qt + 1);
-    const unsigned char* st = smem + stage * STAGE;
-    const unsigned char* sQ = st;
-    const unsigned char* sO = st + RBYTES;
-    const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
-    const int q0 = qt * BQ;
-    const bool active = !CAUSAL || q0 + BQ - 1 >= kw0;
-    if (active) {
-      // ---- S = Q K^T (rows = queries, lane = key), dP = dO V^T ----
-      f32x16 s = cinit, dp = f32x16{};
+  // Each role runs its own loop (a wave only ever runs one of them), so the
+  // two accumulator sets are never live together; both loops meet the same
+  // barriers.
+  f32x16 acc[DB];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + l32 * RPITCH + (16 * ks + 8 * hi) * 2);
-        s = mfma32(a, kf[ks], s);
-      }
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  if (role == 0) {
+    bf16x8 kf[KS];
+    load_frags(k, kf);
+    int stage = 0;
+    for (int qt = qt0; qt < nqt; ++qt, stage ^= 1) {
+      __syncthreads();
+      if (qt + 1 < nqt) load_tile(qt + 1);
+      const unsigned char* st = smem + stage * STAGE;
+      const int q0 = qt * BQ;
+      if (!CAUSAL || q0 + BQ - 1 >= kw0) {
+        f32x16 p = scores(st, kf);
+        probs(p, reinterpret_cast<const float*>(st + 2 * RBYTES), q0);
+        const u32x4 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sO + l32 * RPITCH + (16 * ks + 8 * hi) * 2);
-        dp = mfma32(a, vf[ks], dp);
-      }
-      // ---- P = exp2(t - lse2), dS = P (dP - D) ----
-      const float bj = c2 * float(j - q0 - 4 * hi);  // t = s c1 + bj on the causal side
-      const bool full = CAUSAL && q0 >= kw0 + 31;    // every query of the tile sees every key of the wave
-      f32x16 p, ds;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 L = *reinterpret_cast<const f32x4*>(sL + 8 * g + 4 * hi);
-        const f32x4 Dv = *reinterpret_cast<const f32x4*>(sL + BQ + 8 * g + 4 * hi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const int i = q0 + 8 * g + 4 * hi + e;
-          float t = fmaf(s[r], c1, bj);
-          if (!full) {
-            if (!CAUSAL && j > i) t -= 2.0f * c2 * float(j - i);  // symmetric bias -m |i - j|
-            if (CAUSAL && j > i) t = -__builtin_huge_valf();
-          }
-          const float pr = fast_exp2(t - L[e]);
-          p[r] = pr;
-          ds[r] = pr * (dp[r] - Dv[e]);
+        for (int db = 0; db < DB; ++db) {
+          acc[db] = mfma32(read_tr(st + RBYTES, RPITCH, 0, 32 * db, lane), __builtin_bit_cast(bf16x8, pb0), acc[db]);
+          acc[db] = mfma32(read_tr(st + RBYTES, RPITCH, 16, 32 * db, lane), __builtin_bit_cast(bf16x8, pb1), acc[db]);
         }
       }
-      const u32x4 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
-      const u32x4 sb0 = pack8(ds, 0), sb1 = pack8(ds, 8);
-      // ---- dV^T += dO^T P, dK^T += Q^T dS ----
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dva[db] = mfma32(read_tr(sO, RPITCH, 0, 32 * db, lane), __builtin_bit_cast(bf16x8, pb0), dva[db]);
-        dva[db] = mfma32(read_tr(sO, RPITCH, 16, 32 * db, lane), __builtin_bit_cast(bf16x8, pb1), dva[db]);
-        dka[db] = mfma32(read_tr(sQ, RPITCH, 0, 32 * db, lane), __builtin_bit_cast(bf16x8, sb0), dka[db]);
-        dka[db] = mfma32(read_tr(sQ, RPITCH, 16, 32 * db, lane), __builtin_bit_cast(bf16x8, sb1), dka[db]);
-      }
+      if (qt + 1 < nqt) store_tile(smem + (stage ^ 1) * STAGE);
     }
-    if (qt + 1 < nqt) store_tile(smem + (stage ^ 1) * STAGE);
+  } else {
+    bf16x8 kf[KS], vf[KS];
+    load_frags(k, kf);
+    load_frags(v, vf);
+    int stage = 0;
+    for (int qt = qt0; qt < nqt; ++qt, stage ^= 1) {
+      __syncthreads();
+      if (qt + 1 < nqt) load_tile(qt + 1);
+      const unsigned char* st = smem + stage * STAGE;
+      const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
+      const int q0 = qt * BQ;
+      if (!CAUSAL || q0 + BQ - 1 >= kw0) {
+        f32x16 p = scores(st, kf);
+        f32x16 dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + RBYTES + l32 * RPITCH + (16 * ks + 8 * hi) * 2);
+          dp = mfma32(a, vf[ks], dp);
+        }
+        probs(p, sL, q0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 Dv = *reinterpret_cast<const f32x4*>(sL + BQ + 8 * g + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[4 * g + e] *= dp[4 * g + e] - Dv[e];  // dS = P (dP - D)
+        }
+        const u32x4 sb0 = pack8(p, 0), sb1 = pack8(p, 8);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          acc[db] = mfma32(read_tr(st, RPITCH, 0, 32 * db, lane), __builtin_bit_cast(bf16x8, sb0), acc[db]);
+          acc[db] = mfma32(read_tr(st, RPITCH, 16, 32 * db, lane), __builtin_bit_cast(bf16x8, sb1), acc[db]);
+        }
+      }
+      if (qt + 1 < nqt) store_tile(smem + (stage ^ 1) * STAGE);
+    }
   }
 
-  // ---- epilogue: lane = key j, rows of the accumulators = d ----
+  // ---- epilogue: lane = key j, rows of the accumulator = d ----
   if (j < N) {
+    uint16_t* dst = role == 0 ? dv : dk;
+    const float sc = role == 0 ? 1.0f : scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const long long off = base + (long long)j * D + 32 * db + 8 * g + 4 * hi;
-        u32x2 a, b;
-        a[0] = pack_bf16x2(dka[db][4 * g] * scale, dka[db][4 * g + 1] * scale);
-        a[1] = pack_bf16x2(dka[db][4 * g + 2] * scale, dka[db][4 * g + 3] * scale);
-        b[0] = pack_bf16x2(dva[db][4 * g], dva[db][4 * g + 1]);
-        b[1] = pack_bf16x2(dva[db][4 * g + 2], dva[db][4 * g + 3]);
-        *reinterpret_cast<u32x2*>(dk + off) = a;
-        *reinterpret_cast<u32x2*>(dv + off) = b;
+        u32x2 a;
+        a[0] = pack_bf16x2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc);
+        a[1] = pack_bf16x2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc);
+        *reinterpret_cast<u32x2*>(dst + base + (long long)j * D + 32 * db + 8 * g + 4 * hi) = a;
       }
     }
   }
@@ -416,7 +437,7 @@ hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, 
   const float scale = float(1.0 / std::sqrt(double(D)));
   const int nkb = (a.N + 127) / 128;
   const long long tk = (long long)a.B * a.H * nkb;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(unsigned(tk)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(unsigned(tk)), dim3(512), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
                      nkb, int(tk), a.slopes, c1, scale);
