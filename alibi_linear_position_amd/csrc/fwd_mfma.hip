@@ -108,9 +108,9 @@ __device__ __forceinline__ float bdot2(uint32_t packed, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, one, acc, false);
 }
 
-// One K/V tile of BN keys as the workgroup stages it: each thread holds
-// K_LOADS 16-byte chunks of K (row-major, coalesced) and V_LOADS chunks of V
-// (one key per lane, so the transposed LDS writes of a wave cover whole rows).
+// One K/V tile of BN keys as the workgroup stages it: each thread holds LOADS
+// 16-byte chunks of K (row-major, coalesced) and LOADS chunks of V (the same 8
+// d of LOADS consecutive keys, so the transposed LDS writes are LOADS keys wide).
 template <int D, int NT>
 struct TileRegs {
   static constexpr int BN = 64;
@@ -122,14 +122,15 @@ struct TileRegs {
 
   // Loads of one tile through buffer resources: chunk r of K sits at byte
   // 16 (tid + NT r) of the tile (rows are contiguous), chunk r of V at byte
-  // 2 (key D + 8 (tid / BN + (NT / BN) r)). Each thread's byte offset is fixed
+  // 2 ((LOADS (tid % KG) + r) D + 8 (tid / KG)). Each thread's byte offset is fixed
   // and the tile's byte offset `tb` is a scalar, so a load carries no per-tile
   // vector address arithmetic. A resource whose range ends at row Nk makes
   // rows past it read as zero when the tile starts at the resource's base
   // (tb = 0: the range check covers the vector offset).
   static __device__ __forceinline__ uint32_t k_off(int tid) { return uint32_t(tid) * 16u; }
+  static constexpr int KG = BN / LOADS;  // V: groups of LOADS consecutive keys
   static __device__ __forceinline__ uint32_t v_off(int tid) {
-    return (uint32_t(tid % BN) * D + uint32_t(tid / BN) * 8u) * 2u;
+    return (uint32_t(tid % KG) * LOADS * D + uint32_t(tid / KG) * 8u) * 2u;
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t tb,
                                        uint32_t koff, uint32_t voff) {
@@ -138,10 +139,15 @@ struct TileRegs {
       k[r] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, int(tb + uint32_t(NT * 16 * r)), 0));
       v[r] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, int(tb + uint32_t((NT / BN) * 16 * r)), 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, int(tb + uint32_t(r * D * 2)), 0));
     }
   }
 
+  // K rows go to LDS as loaded. V goes transposed, V^T[d][key], with the key
+  // order of each 16-key group permuted (perm16) to match the accumulator
+  // layout of P^T: a thread holds the same 8 d of LOADS consecutive keys, so
+  // for every d it writes their LOADS values as one 2 LOADS-byte store (the
+  // keys of a 4-group stay contiguous under perm16).
   template <int KPITCH, int VPITCH>
   __device__ __forceinline__ void store(unsigned char* sK, unsigned char* sV, int tid) const {
 #pragma unroll
@@ -149,14 +155,24 @@ struct TileRegs {
       const int c = tid + NT * r;
       const int row = c / CPR, col = c % CPR;
       *reinterpret_cast<u32x4*>(sK + row * KPITCH + col * 16) = k[r];
-      const int key = tid % BN;
-      const int vcol = tid / BN + (NT / BN) * r;
-      const int pos = (key & ~15) | perm16(key & 15);
-      unsigned char* dst = sV + (vcol * 8) * VPITCH + pos * 2;
+    }
+    const int key = (tid % KG) * LOADS, vcol = tid / KG;
+    const int pos = (key & ~15) | perm16(key & 15);
+    unsigned char* dst = sV + (vcol * 8) * VPITCH + pos * 2;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint16_t*>(dst + (2 * e) * VPITCH) = uint16_t(v[r][e] & 0xffffu);
-        *reinterpret_cast<uint16_t*>(dst + (2 * e + 1) * VPITCH) = uint16_t(v[r][e] >> 16);
+    for (int e = 0; e < 8; ++e) {
+      // bf16 e of each key: the low (even e) or high (odd e) half of word e / 2
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      if constexpr (LOADS == 4) {
+        u32x2 w;
+        w[0] = __builtin_amdgcn_perm(v[1][e >> 1], v[0][e >> 1], sel);
+        w[1] = __builtin_amdgcn_perm(v[3][e >> 1], v[2][e >> 1], sel);
+        *reinterpret_cast<u32x2*>(dst + e * VPITCH) = w;
+      } else if constexpr (LOADS == 2) {
+        *reinterpret_cast<uint32_t*>(dst + e * VPITCH) = __builtin_amdgcn_perm(v[1][e >> 1], v[0][e >> 1], sel);
+      } else {
+        static_assert(LOADS == 1, "1, 2 or 4 keys per thread");
+        *reinterpret_cast<uint16_t*>(dst + e * VPITCH) = uint16_t((e & 1) ? v[0][e >> 1] >> 16 : v[0][e >> 1]);
       }
     }
   }
