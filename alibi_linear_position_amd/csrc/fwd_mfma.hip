@@ -290,7 +290,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     // through resources that start at the tile, so missing rows read as zero.
     // With no tile to visit (every query before every key) tile 0 is staged
     // and never read.
-    const int jp = max(ntiles - 1, 0) * BN;
+    int first = ntiles - 1;
+    if (!CAUSAL && Nk % BN == 0) {  // the order of the loops below
+      const int x = q0 + delta + 1, nfull = Nk / BN;
+      const int tl = x < BN ? -1 : min(x / BN - 1, nfull - 1);
+      const int ql = q0 + BM - 1 + delta;
+      const int tr = max(tl + 1, ql <= 0 ? 0 : (ql + BN - 1) / BN);
+      const int mid_hi = min(tr, nfull) - 1;
+      first = mid_hi > tl ? mid_hi : (tr < nfull ? tr : tl);
+    }
+    const int jp = max(first, 0) * BN;
     regs.load(rsrc(k + kbase + (long long)jp * D, Nk - jp), rsrc(v + kbase + (long long)jp * D, Nk - jp), 0u,
               koff, voff);
     regs.template store<KPITCH, VPITCH>(smem, smem + KBYTES, tid);
@@ -366,12 +375,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // of the next tile (whose global loads were issued at the top). MASKED tiles
   // may hold keys past a query or past Nk; the others hold none for any wave.
   int stage = 0;
-  auto step = [&](int tile, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // kind 0: tile needing the mask (or past Nk); 1: every key at or before
+  // every query; 2 (no causal mask only): every key at or after every query.
+  auto step = [&](int tile, int next, auto kind_tag) {
+    constexpr int KIND = decltype(kind_tag)::value;
+    constexpr bool MASKED = KIND == 0;
+    constexpr bool RIGHT = KIND == 2;
     const int j0 = tile * BN;
     // Stage `stage` holds this tile; every wave is done with the other stage.
     __syncthreads();
-    if (tile > 0) regs.load(rk, rv, uint32_t(j0 - BN) * (D * 2), koff, voff);  // in flight during this tile
+    if (next >= 0) regs.load(rk, rv, uint32_t(next) * (BN * D * 2), koff, voff);  // in flight during this tile
     const unsigned char* sK = smem + stage * STAGE;
     const unsigned char* sV = sK + KBYTES;
     unsigned char* const sKn = smem + (stage ^ 1) * STAGE;
@@ -402,6 +415,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     // row sum taken from the same bf16 values.
     u32x4 pf[PS];
     const float sc = VAR == 0 ? c1 : 1.0f;
+    // Keys after the query (RIGHT) carry -c2 (j - pi): relative to the seed
+    // this is the bias of the mirrored key minus 2 c2 (8 (r / 4) + r % 4).
     auto exp_block = [&](float b0, float b1) {
       float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
 #pragma unroll
@@ -413,7 +428,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
           for (int e = 0; e < 4; ++e) {
             const int r0 = 8 * half + 2 * e;
             const float bb = kb ? b1 : b0;
-            pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], sc, bb)), fast_exp2(fmaf(s[kb][r0 + 1], sc, bb)));
+            float bb0 = bb, bb1 = bb;
+            if constexpr (RIGHT && VAR == 0) {
+              bb0 = fmaf(-2.0f * c2, float(8 * (r0 >> 2) + (r0 & 3)), bb);
+              bb1 = fmaf(-2.0f * c2, float(8 * (r0 >> 2) + (r0 & 3) + 1), bb);
+            }
+            pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], sc, bb0)), fast_exp2(fmaf(s[kb][r0 + 1], sc, bb1)));
             lpart[e] = bdot2(pk[e], lpart[e]);
           }
           pf[2 * kb + half] = pk;
@@ -441,11 +461,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       // exponentiate against it directly. A lane whose partial row sum leaves
       // (0, kOptLimit] (a score above the maximum by ~2^11, an overflow, or a
       // row without a finite maximum yet) sends the wave through the bound and
-      // the rescale, and the tile is redone.
-      lsum = exp_block(bt0 - m_run, bt1 - m_run);
+      // the rescale, and the tile is redone. Right of the queries the bias of
+      // block kb is at most -bt_kb (its first key), left of them at most bt_kb
+      // + 31 c2, which the seed already carries.
+      const float a0 = RIGHT ? -bt0 : bt0, a1 = RIGHT ? -bt1 : bt1;
+      lsum = exp_block(a0 - m_run, a1 - m_run);
       if (__builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit))) {
-        rescale(max_xor32(fmaxf(fmaf(max16(s[0]), c1, bt0), fmaf(max16(s[1]), c1, bt1))));
-        lsum = exp_block(bt0 - m_run, bt1 - m_run);
+        rescale(max_xor32(fmaxf(fmaf(max16(s[0]), c1, a0), fmaf(max16(s[1]), c1, a1))));
+        lsum = exp_block(a0 - m_run, a1 - m_run);
       }
     } else {
       float mcand;
@@ -501,14 +524,31 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // position q0 + delta (so before every wave's queries) and lie wholly below
   // Nk: no mask. The rest, at most (BM + BN - 1) / BN + 1 of them under the
   // causal mask, take the masked path; without the mask every tile does.
-  int t_open = -1;
+  using Masked = std::integral_constant<int, 0>;
+  using Left = std::integral_constant<int, 1>;
+  using Right = std::integral_constant<int, 2>;
+  const int x = q0 + delta + 1;  // keys [0, x) are at or before every query of the block
   if (CAUSAL) {
-    const int x = q0 + delta + 1;                      // keys [0, x) are visible to every query
-    t_open = x < BN ? -1 : min(min(x / BN - 1, Nk / BN - 1), ntiles - 1);
+    const int t_open = x < BN ? -1 : min(min(x / BN - 1, Nk / BN - 1), ntiles - 1);
+    int tile = ntiles - 1;
+    for (; tile > t_open; --tile) step(tile, tile - 1, Masked{});
+    for (; tile > t_dead; --tile) step(tile, tile - 1, Left{});
+  } else {
+    // Without the mask: the tiles around the diagonal and a partial last tile
+    // first (masked path), then the tiles wholly after the block's queries
+    // nearest first, then those wholly before them nearest first, so the
+    // running maximum is set early and the bias only falls afterwards.
+    const int nfull = Nk / BN;
+    const int tl = x < BN ? -1 : min(x / BN - 1, nfull - 1);   // left tiles 0 .. tl
+    const int ql = q0 + BM - 1 + delta;                          // last query position of the block
+    const int tr = max(tl + 1, ql <= 0 ? 0 : (ql + BN - 1) / BN);  // right tiles tr .. nfull - 1
+    const int mid_hi = min(tr, nfull) - 1;                        // middle tiles tl + 1 .. mid_hi
+    const int after_mid = tr < nfull ? tr : tl;
+    if (Nk % BN != 0) step(nfull, mid_hi > tl ? mid_hi : after_mid, Masked{});
+    for (int t = mid_hi; t > tl; --t) step(t, t - 1 > tl ? t - 1 : after_mid, Masked{});
+    for (int t = tr; t < nfull; ++t) step(t, t + 1 < nfull ? t + 1 : tl, Right{});
+    for (int t = tl; t >= 0; --t) step(t, t - 1, Left{});
   }
-  int tile = ntiles - 1;
-  for (; tile > t_open; --tile) step(tile, std::true_type{});
-  for (; tile > t_dead; --tile) step(tile, std::false_type{});
 
   // ---- epilogue: O / l -> bf16; a row that saw no key gives 0 ----
   const float lt = sum_xor32(l_run);
