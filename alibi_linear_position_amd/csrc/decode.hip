@@ -20,7 +20,7 @@ namespace alibi {
 namespace {
 
 constexpr int kDecodeThreads = 256;
-constexpr int kDecodeUnroll = 4;
+constexpr int kDecodeUnroll = 8;
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
 template <int LPK>
@@ -182,10 +182,10 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, void* out
 
 void decode_plan(int B, int H, int L, int d, int* splits, int* chunk) {
   (void)d;
-  // Aim for about 2048 workgroups (8 per CU on 256 CUs) so every CU has enough
+  // Aim for about 4096 workgroups (16 per CU on 256 CUs) so every CU has enough
   // loads in flight; never cut a range below 256 keys.
   const long long bh = (long long)B * H;
-  long long s = (2048 + bh - 1) / bh;
+  long long s = (4096 + bh - 1) / bh;
   const long long max_s = (L + 255) / 256;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
