@@ -99,10 +99,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int role = wave >> 2;  // 0: dV, 1: dK
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int w = blockIdx.x;
-  const int lw = (total & 7) == 0 ? (w & 7) * (total >> 3) + (w >> 3) : w;
-  const int bh = lw / nkb;
-  const int kblk = lw - bh * nkb;  // low key blocks see the most queries: scheduled first
+  const WgBlock wb = schedule_block(blockIdx.x, total / nkb, nkb);
+  const int bh = wb.bh;
+  const int kblk = wb.rank;  // low key blocks see the most queries: scheduled first
   const int h = bh % H;
   const float c2 = slopes[h] * kLog2e;
   const float c21 = c2 / c1;
@@ -293,10 +292,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int w = blockIdx.x;
-  const int lw = (total & 7) == 0 ? (w & 7) * (total >> 3) + (w >> 3) : w;
-  const int bh = lw / nqb;
-  const int qblk = nqb - 1 - (lw - bh * nqb);
+  const WgBlock wb = schedule_block(blockIdx.x, total / nqb, nqb);
+  const int bh = wb.bh;
+  const int qblk = nqb - 1 - wb.rank;  // high query blocks see the most keys: scheduled first
   const int h = bh % H;
   const float c2 = slopes[h] * kLog2e;
   const float c21 = c2 / c1;

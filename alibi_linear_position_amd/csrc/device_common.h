@@ -59,6 +59,25 @@ __device__ __forceinline__ bf16x8 read_tr(const unsigned char* tile, int pitch, 
   return __builtin_bit_cast(bf16x8, v8);
 }
 
+// Workgroup w -> ((b, h) pair, block rank) for nbh pairs of nblk blocks each.
+// Workgroups are dealt round-robin to the 8 XCDs (w % 8). With nbh a multiple
+// of 8 every XCD gets whole (b, h) pairs, so a head's K and V stay in that
+// XCD's L2, and runs them rank by rank: rank 0 (the caller's heaviest block)
+// of all its pairs first, so no heavy block starts late. Otherwise ranks still
+// go in order over all pairs.
+struct WgBlock {
+  int bh;
+  int rank;
+};
+__device__ __forceinline__ WgBlock schedule_block(int w, int nbh, int nblk) {
+  if ((nbh & 7) == 0) {
+    const int per = nbh >> 3;  // pairs per XCD
+    const int x = w >> 3;      // position in the XCD's queue
+    return {(w & 7) * per + x % per, x / per};
+  }
+  return {w % nbh, w / nbh};
+}
+
 // Butterfly reductions over the full 64-lane wave.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -229,11 +229,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Workgroup -> (b, h, query block): XCD-grouped, heaviest block first.
-  const int w = blockIdx.x;
-  const int lw = (total & 7) == 0 ? (w & 7) * (total >> 3) + (w >> 3) : w;
-  const int bh = lw / nqb;
-  const int qblk = nqb - 1 - (lw - bh * nqb);
+  // Workgroup -> (b, h, query block): heads kept per XCD, the heaviest (last)
+  // query blocks of every head first.
+  const WgBlock wb = schedule_block(blockIdx.x, total / nqb, nqb);
+  const int bh = wb.bh;
+  const int qblk = nqb - 1 - wb.rank;
   const int h = bh % H;
   const float mh = slopes[h];
   const float c2 = mh * kLog2e;
