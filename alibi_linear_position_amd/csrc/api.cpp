@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "launch.h"
+#include "device_common.h"
 
 namespace {
 
@@ -252,6 +253,15 @@ int alibi_attn_weights_f32(const float* q, const float* k, float* w, int B, int 
   if (causal != 0 && causal != 1) return ALIBI_EINVAL;
   if (N > 1024 || d > 256) return ALIBI_ENOTSUP;
   return hip_status(alibi::launch_weights_f32(q, k, w, B, H, N, d, slopes, causal, scale_log2(d), stream));
+}
+
+int alibi_debug_schedule(int w, int nbh, int nblk, int* out2) {
+  if (out2 == nullptr || nbh < 1 || nblk < 1 || w < 0 || (long long)w >= (long long)nbh * nblk)
+    return ALIBI_EINVAL;
+  const alibi::WgBlock b = alibi::schedule_block(w, nbh, nblk);
+  out2[0] = b.bh;
+  out2[1] = b.rank;
+  return ALIBI_OK;
 }
 
 const char* alibi_status_string(int status) {

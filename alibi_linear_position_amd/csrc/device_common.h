@@ -62,18 +62,34 @@ __device__ __forceinline__ bf16x8 read_tr(const unsigned char* tile, int pitch, 
 // Workgroup w -> ((b, h) pair, block rank) for nbh pairs of nblk blocks each.
 // Workgroups are dealt round-robin to the 8 XCDs (w % 8). With nbh a multiple
 // of 8 every XCD gets whole (b, h) pairs, so a head's K and V stay in that
-// XCD's L2, and runs them rank by rank: rank 0 (the caller's heaviest block)
-// of all its pairs first, so no heavy block starts late. Otherwise ranks still
-// go in order over all pairs.
+// XCD's L2, and walks them in groups of kSchedGroup pairs, rank by rank inside
+// a group: rank 0 (the caller's heaviest block) of the group's pairs first.
+// Few pairs in flight keep the XCD's L2 on their K and V, and rank order keeps
+// heavy blocks from starting late. Otherwise ranks go in order over all pairs.
+// Host and device: the host side is checked to be a bijection.
+constexpr int kSchedGroup = 4;
 struct WgBlock {
   int bh;
   int rank;
 };
-__device__ __forceinline__ WgBlock schedule_block(int w, int nbh, int nblk) {
+__host__ __device__ inline WgBlock schedule_block(int w, int nbh, int nblk) {
   if ((nbh & 7) == 0) {
     const int per = nbh >> 3;  // pairs per XCD
-    const int x = w >> 3;      // position in the XCD's queue
-    return {(w & 7) * per + x % per, x / per};
+    const int x = w >> 3;      // position in this XCD's queue, 0 .. per * nblk - 1
+    const int G = per < kSchedGroup ? per : kSchedGroup;
+    const int full = per / G;  // complete groups of G pairs
+    const int span = G * nblk;
+    int g, gsize, in;
+    if (x < full * span) {
+      g = x / span;
+      gsize = G;
+      in = x - g * span;
+    } else {  // the last, smaller group
+      g = full;
+      gsize = per - full * G;
+      in = x - full * span;
+    }
+    return {(w & 7) * per + g * G + in % gsize, in / gsize};
   }
   return {w % nbh, w / nbh};
 }

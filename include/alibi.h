@@ -231,6 +231,15 @@ int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out,
 #define ALIBI_SLOPES_EXPLICIT 4
 int alibi_slopes_recipe(int recipe, int H, int log_distance, float* slopes_out);
 
+/*
+ * TEST ONLY, host only: the workgroup -> ((b, h) pair, block rank) schedule the
+ * forward and backward kernels use (heads kept per XCD, heaviest blocks first
+ * within small groups of heads), for workgroup w of nbh pairs x nblk blocks.
+ * Writes {pair, rank} to out2 (host array of 2 ints). ALIBI_EINVAL for w
+ * outside [0, nbh nblk), sizes < 1 or NULL.
+ */
+int alibi_debug_schedule(int w, int nbh, int nblk, int* out2);
+
 /* Static, never-NULL description of a status code. */
 const char* alibi_status_string(int status);
 

@@ -192,3 +192,22 @@ def test_fwd_ex_validation(lib):
     assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", q=FAKE + 2, d=16) == -1
     assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", d=300) == -2
     assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", opts=O(16, 0.0, 0.0, 0, 0), d=16) == -1
+
+
+@pytest.mark.parametrize("nbh", [1, 3, 7, 8, 12, 16, 24, 32, 40, 64, 128, 136, 512])
+@pytest.mark.parametrize("nblk", [1, 2, 5, 32, 64])
+def test_workgroup_schedule_is_a_bijection(lib, nbh, nblk):
+    # every workgroup index must land on a distinct, in-range (pair, block):
+    # the kernels index q/k/v/out with it
+    out = (ctypes.c_int * 2)()
+    seen = set()
+    for w in range(nbh * nblk):
+        assert lib.alibi_debug_schedule(w, nbh, nblk, out) == 0
+        bh, rank = out[0], out[1]
+        assert 0 <= bh < nbh and 0 <= rank < nblk, (w, bh, rank)
+        seen.add((bh, rank))
+        if nbh % 8 == 0:
+            per = nbh // 8
+            assert bh // per == w % 8            # the pair stays on workgroup w's XCD
+    assert len(seen) == nbh * nblk
+    assert lib.alibi_debug_schedule(nbh * nblk, nbh, nblk, out) == -1
