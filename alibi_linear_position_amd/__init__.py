@@ -41,6 +41,7 @@ EXPORTS = {
     "alibi_attn_fwd_ex_f32": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P],
     "alibi_slopes_recipe": [_I, _I, _I, _P],
     "alibi_debug_schedule": [_I, _I, _I, _P],
+    "alibi_debug_fwd_waves": [_I],
     "alibi_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
     "alibi_status_string": [_I],
     "alibi_release": [],

@@ -264,6 +264,12 @@ int alibi_debug_schedule(int w, int nbh, int nblk, int* out2) {
   return ALIBI_OK;
 }
 
+int alibi_debug_fwd_waves(int nw) {
+  if (nw != 0 && nw != 4 && nw != 8) return ALIBI_EINVAL;
+  alibi::set_fwd_waves(nw);
+  return ALIBI_OK;
+}
+
 const char* alibi_status_string(int status) {
   switch (status) {
     case ALIBI_OK: return "ALIBI_OK: success";

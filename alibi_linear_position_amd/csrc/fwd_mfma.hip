@@ -11,10 +11,10 @@
 //
 // Layout of the work
 // ------------------
-// * A workgroup is NW waves (4 by default) and owns BM = 32 NW consecutive
-//   query rows of one (b, h); each wave owns 32 rows. Two waves share each SIMD
-//   (at most 256 registers per lane; two 4-wave workgroups per CU), so one
-//   wave's MFMA work can overlap the other's softmax arithmetic.
+// * A workgroup is NW = 4 or 8 waves and owns BM = 32 NW consecutive query
+//   rows of one (b, h); each wave owns 32 rows. Two waves share each SIMD (at
+//   most 256 registers per lane; two 4-wave or one 8-wave workgroup per CU), so
+//   one wave's MFMA work can overlap the other's softmax arithmetic.
 // * Key/value tiles of BN = 64 rows are staged HBM -> registers -> LDS by the
 //   whole workgroup: K row-major (16-byte coalesced loads, rows padded by 16 B
 //   against bank conflicts), V transposed to V^T[d][key] (one key per lane,
@@ -51,6 +51,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <atomic>
 #include <cstdlib>
 #include <type_traits>
 
@@ -58,14 +59,27 @@ namespace alibi {
 
 namespace {
 
-// Waves per workgroup: 4 by default (two workgroups share a CU);
-// ALIBI_FWD_NW=8 selects one 8-wave workgroup per CU (tuning only).
-int fwd_waves() {
-  static const int nw = [] {
+// Forced waves per workgroup: 0 = automatic, else 4 or 8 (ALIBI_FWD_NW at
+// load time, or set_fwd_waves).
+std::atomic<int>& waves_override() {
+  static std::atomic<int> w{[] {
     const char* e = std::getenv("ALIBI_FWD_NW");
-    return (e != nullptr && std::atoi(e) == 8) ? 8 : 4;
-  }();
-  return nw;
+    const int n = e != nullptr ? std::atoi(e) : 0;
+    return (n == 4 || n == 8) ? n : 0;
+  }()};
+  return w;
+}
+
+// Waves per workgroup. Two waves share each SIMD either way; 8 waves (one
+// workgroup per CU) halve the K/V staging per query row and measure faster for
+// d = 128, while d = 64, soft capping (more VALU work per score) and grids of
+// fewer than two 8-wave workgroups per CU run better as two 4-wave workgroups.
+int fwd_waves(const FwdArgs& a, int flags) {
+  const int o = waves_override().load(std::memory_order_relaxed);
+  if (o != 0) return o;
+  if (a.d != 128 || (flags & 4) != 0) return 4;
+  const long long wg8 = (long long)a.B * a.H * ((a.Nq + 255) / 256);
+  return wg8 >= 512 ? 8 : 4;
 }
 constexpr float kLazy = 8.0f;
 // Largest partial row sum (32 keys of one lane) accepted without a fresh bound.
@@ -580,24 +594,31 @@ hipError_t launch_cfg(const FwdArgs& a, float c1, const FwdVariant& var, hipStre
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_var(const FwdArgs& a, int flags, bool ext, float c1, const FwdVariant& var, hipStream_t s) {
+template <int D, bool CAUSAL, int NW>
+hipError_t launch_var_nw(const FwdArgs& a, int flags, bool ext, float c1, const FwdVariant& var, hipStream_t s) {
   switch (flags) {
     case 0:
-      if (ext) return launch_cfg<D, 4, CAUSAL, 0, true>(a, c1, var, s);
-      return fwd_waves() == 8 ? launch_cfg<D, 8, CAUSAL, 0, false>(a, c1, var, s)
-                              : launch_cfg<D, 4, CAUSAL, 0, false>(a, c1, var, s);
-    case 1: return launch_cfg<D, 4, CAUSAL, 1, true>(a, c1, var, s);
-    case 2: return launch_cfg<D, 4, CAUSAL, 2, true>(a, c1, var, s);
-    case 3: return launch_cfg<D, 4, CAUSAL, 3, true>(a, c1, var, s);
-    case 4: return launch_cfg<D, 4, CAUSAL, 4, true>(a, c1, var, s);
-    case 5: return launch_cfg<D, 4, CAUSAL, 5, true>(a, c1, var, s);
-    case 6: return launch_cfg<D, 4, CAUSAL, 6, true>(a, c1, var, s);
-    default: return launch_cfg<D, 4, CAUSAL, 7, true>(a, c1, var, s);
+      return ext ? launch_cfg<D, NW, CAUSAL, 0, true>(a, c1, var, s)
+                 : launch_cfg<D, NW, CAUSAL, 0, false>(a, c1, var, s);
+    case 1: return launch_cfg<D, NW, CAUSAL, 1, true>(a, c1, var, s);
+    case 2: return launch_cfg<D, NW, CAUSAL, 2, true>(a, c1, var, s);
+    case 3: return launch_cfg<D, NW, CAUSAL, 3, true>(a, c1, var, s);
+    case 4: return launch_cfg<D, NW, CAUSAL, 4, true>(a, c1, var, s);
+    case 5: return launch_cfg<D, NW, CAUSAL, 5, true>(a, c1, var, s);
+    case 6: return launch_cfg<D, NW, CAUSAL, 6, true>(a, c1, var, s);
+    default: return launch_cfg<D, NW, CAUSAL, 7, true>(a, c1, var, s);
   }
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_var(const FwdArgs& a, int flags, bool ext, float c1, const FwdVariant& var, hipStream_t s) {
+  return fwd_waves(a, flags) == 4 ? launch_var_nw<D, CAUSAL, 4>(a, flags, ext, c1, var, s)
+                                  : launch_var_nw<D, CAUSAL, 8>(a, flags, ext, c1, var, s);
+}
+
 }  // namespace
+
+void set_fwd_waves(int nw) { waves_override().store(nw, std::memory_order_relaxed); }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hipStream_t stream) {
   FwdVariant var;

@@ -57,6 +57,16 @@ def decode_bytes(B, H, L, d):
     return 2.0 * B * H * L * d * 2 + 2.0 * B * H * d * 2
 
 
+def fwd_waves(B, H, N, d):
+    """Waves per workgroup of the plain bf16 forward launch, as the library picks
+    them: ALIBI_FWD_NW when set to 4 or 8, else 8 for d = 128 when the grid has at
+    least 512 eight-wave workgroups, else 4."""
+    env = os.environ.get("ALIBI_FWD_NW")
+    if env in ("4", "8"):
+        return int(env)
+    return 8 if d == 128 and B * H * ((N + 255) // 256) >= 512 else 4
+
+
 def traffic_bytes(profile_md, sources, root=ROOT):
     """HBM bytes per launch from a committed counter summary, or None.
 
@@ -203,7 +213,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes("fwd_mfma_B8_H16_N4096_d128.md", ["fwd_mfma.hip", "device_common.h"]),
-                     "kernel": f"fwd_mfma_kernel<128,{os.environ.get('ALIBI_FWD_NW', '4')},true,0,false>", "ms_per_launch": round(t_fwd * 1e3, 4),
+                     "kernel": f"fwd_mfma_kernel<128,{fwd_waves(fw.B, fw.H, fw.N, fw.d)},true,0,false>",
+                     "ms_per_launch": round(t_fwd * 1e3, 4),
                      "per_launch": f"{flops:.4e} flop"},
         "decode": {"value": round(gbs, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,

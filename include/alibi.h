@@ -240,6 +240,19 @@ int alibi_slopes_recipe(int recipe, int H, int log_distance, float* slopes_out);
  */
 int alibi_debug_schedule(int w, int nbh, int nblk, int* out2);
 
+/*
+ * TEST AND TUNING ONLY: waves per workgroup of the bf16 MFMA forward kernel,
+ * process-wide. 0 = automatic (the default: 8 for d = 128 without soft capping
+ * when the grid has at least 512 eight-wave workgroups, else 4), 4 or 8 =
+ * forced for every later call. The two differ only by rounding: a row's tiles
+ * are visited in the same order, but which of them take the exact or the
+ * bounded running maximum depends on the block height. The environment variable
+ * ALIBI_FWD_NW=4|8, read once at load, sets the same override. Not
+ * synchronised with launches in flight on other threads. ALIBI_EINVAL for
+ * other values.
+ */
+int alibi_debug_fwd_waves(int nw);
+
 /* Static, never-NULL description of a status code. */
 const char* alibi_status_string(int status);
 

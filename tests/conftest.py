@@ -30,3 +30,13 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(params=[4, 8], ids=["nw4", "nw8"])
+def fwd_waves(request):
+    """Forces 4- or 8-wave workgroups in the bf16 forward kernel for one test."""
+    import alibi_linear_position_amd as alibi
+    lib = alibi.load_library()
+    assert lib.alibi_debug_fwd_waves(request.param) == 0
+    yield request.param
+    assert lib.alibi_debug_fwd_waves(0) == 0

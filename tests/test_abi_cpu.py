@@ -211,3 +211,12 @@ def test_workgroup_schedule_is_a_bijection(lib, nbh, nblk):
             assert bh // per == w % 8            # the pair stays on workgroup w's XCD
     assert len(seen) == nbh * nblk
     assert lib.alibi_debug_schedule(nbh * nblk, nbh, nblk, out) == -1
+
+
+def test_fwd_waves_override_validation(lib):
+    # host-only setter: 0 (automatic), 4 and 8 are accepted, anything else refused
+    for nw in (4, 8, 0):
+        assert lib.alibi_debug_fwd_waves(nw) == 0
+    for nw in (-1, 1, 2, 6, 16):
+        assert lib.alibi_debug_fwd_waves(nw) == -1
+    assert lib.alibi_debug_fwd_waves(0) == 0

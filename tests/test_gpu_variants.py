@@ -85,7 +85,7 @@ def _bf16_case(alibi, shape_q, shape_kv, slopes, causal, clamp, logd, cap, qo=0,
 @pytest.mark.parametrize("flags", FLAGS, ids=_ids)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
-def test_bf16_mfma_variants(alibi, flags, d, causal):
+def test_bf16_mfma_variants(alibi, fwd_waves, flags, d, causal):
     clamp, logd, cap = flags
     cap = None if cap is None else 5.0
     clamp = None if clamp is None else -10.0
@@ -114,7 +114,7 @@ def test_bf16_paper_settings_with_recipes(alibi, recipe):
     (64, 64, 4096, 4096, True),  # both offsets shifted
 ])
 @pytest.mark.parametrize("d", [64, 128])
-def test_bf16_mfma_offsets(alibi, Nq, Nk, qo, ko, causal, d):
+def test_bf16_mfma_offsets(alibi, fwd_waves, Nq, Nk, qo, ko, causal, d):
     s = oracle.slopes_ref(2)
     out, ref = _bf16_case(alibi, (2, 2, Nq, d), (2, 2, Nk, d), s, causal, None, False, None, qo, ko)
     check_bf16(out, ref, f"mfma offsets {Nq},{Nk},{qo},{ko},{causal} d={d}")
@@ -123,7 +123,7 @@ def test_bf16_mfma_offsets(alibi, Nq, Nk, qo, ko, causal, d):
     assert np.all(got[zero_rows] == 0.0)
 
 
-def test_bf16_offsets_with_all_mitigations(alibi):
+def test_bf16_offsets_with_all_mitigations(alibi, fwd_waves):
     s = oracle.slopes_recipe_ref("wide", 3)
     out, ref = _bf16_case(alibi, (1, 3, 90, 128), (1, 3, 400, 128), s, True, -20.0, True, 8.0, 310, 0)
     check_bf16(out, ref, "mfma chunk + all mitigations")
