@@ -13,12 +13,14 @@
 // * bwd_prep_kernel: D_i and the log-sum-exp in log2 units, one lane group
 //   per row.
 // * bwd_dkdv_kernel: one workgroup per 128 keys of one (b, h), eight waves:
-//   four own dV and four own dK of 32 keys each, keeping their keys' K (and V)
+//   four own dV and four own dK of 32 keys each, keeping their keys' K (or V)
 //   rows as MFMA B operands in registers. Query tiles of 32 rows stream
-//   through LDS (double-buffered), row-major: read straight for S = Q K^T and
+//   through a three-stage LDS ring: read straight for S = Q K^T and
 //   dP = dO V^T (rows = queries, lane = key), and read transposed
 //   (ds_read_b64_tr_b16) for dV^T += dO^T P and dK^T += Q^T dS, so P and dS go
-//   from registers to the next MFMA as B operands.
+//   from registers to the next MFMA as B operands. The dV waves compute P once
+//   and hand it to the dK waves through LDS; the dK waves run one query tile
+//   behind, so both roles work at the same time between barriers.
 // * bwd_dq_kernel: one workgroup per 128 queries, the forward's layout:
 //   S^T = K Q^T and dP^T = V dO^T (lane = query, so lse and D are one value
 //   per lane), dS^T packed to bf16 and dQ^T += K^T dS^T, with K^T read
@@ -39,6 +41,71 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family parts:
+// 32-bit data format, byte-granular range check against the record count.
+constexpr int kBufferFlags = 0x00020000;
+
+// Buffer resource over `rows` rows of D bf16 (capped at 2^32 - 1 bytes, which
+// no valid 16-byte chunk reaches): loads at or past the end read as zero. The
+// range check covers the vector offset, so tile offsets go there.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* p, long long rows) {
+  const uint32_t bytes = uint32_t(min(rows * D * 2, 0xffffffffLL));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, int(bytes), kBufferFlags);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Row-major bf16 tile in LDS, D / 8 16-byte chunks per row and no padding:
+// chunk c of row r sits at chunk position c ^ x(r). The XOR pattern (a
+// function of r % 16) keeps both read patterns of the backward kernels free of
+// LDS bank conflicts (64 banks of 4 bytes): 16 consecutive rows read at one
+// chunk with 16-byte reads, and 4 consecutive rows x 4 chunks per 32 lanes
+// with ds_read_b64_tr_b16. (Row padding cannot serve both: the 16-byte row
+// reads need a row stride of 4 banks times an odd number, the transposed reads
+// a multiple of 16 banks.)
+template <int D>
+struct SwzTile {
+  static constexpr int ROWB = 2 * D;
+  static __host__ __device__ constexpr int x(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+  // byte offset of chunk c of row r
+  static __device__ __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ x(r)) << 4); }
+  // 16-byte row reads: lane l reads row r0 + l % 32 (r0 a multiple of 16),
+  // chunk 2 ks + l / 32, at r0 ROWB + (row_base(l) ^ 32 ks).
+  static __device__ __forceinline__ int row_base(int lane) {
+    const int r = lane & 31, hi = lane >> 5;
+    return r * ROWB | ((hi ^ x(r)) << 4);
+  }
+  // Transposed reads (read_tr below): the two per-lane bases, for tile rows
+  // +{0..3} (+4 for lanes >= 32) and +{8..11} (+4).
+  static __device__ __forceinline__ int tr_base(int lane, int second) {
+    const int j = lane & 15, g = (lane >> 4) & 1, hi = lane >> 5;
+    const int r = 4 * hi + (j >> 2) + 8 * second;
+    return r * ROWB | ((((2 * g) | ((j & 3) >> 1)) ^ x(r)) << 4) | (8 * (j & 1));
+  }
+};
+
+// MFMA A operand (rows = 32 d values, k = 16 rows of a swizzled row-major LDS
+// tile) read transposed with ds_read_b64_tr_b16: within each 16-lane group,
+// lanes 4e .. 4e + 3 point at 8-byte pieces of tile row e and lane j receives
+// column j of those 4 rows. Lane l gets d = dcol + l % 32 (dcol a multiple of
+// 32) and tile rows r16 + {0..3, 8..11} (l < 32) or r16 + {4..7, 12..15}
+// (l >= 32), r16 a multiple of 16: the row order of the 32x32 accumulator
+// layout, so an accumulator used as the B operand pairs each of its rows with
+// the matching tile row. tb0, tb1: SwzTile<D>::tr_base(lane, 0 / 1).
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const unsigned char* tile, int tb0, int tb1, int r16, int dcol) {
+  const int m = (dcol >> 5) << 6;  // chunk 4 (dcol / 32): XOR 64 (dcol / 32) on the byte offset
+  const unsigned char* t = tile + r16 * SwzTile<D>::ROWB;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (tb0 ^ m)));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (tb1 ^ m)));
+  const short v8 __attribute__((ext_vector_type(8))) = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v8);
+}
 
 // Pack 8 fp32 values (registers base .. base + 7 of an accumulator) to bf16.
 __device__ __forceinline__ u32x4 pack8(const f32x16& x, int base) {
@@ -76,10 +143,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 
 // ---------------------------------------------------------------- dK, dV ----
 // Eight waves: waves 0-3 own dV and waves 4-7 own dK of the same 4 x 32 keys
-// (waves w and w + 4 share a SIMD). A dV wave computes S and P and
-// accumulates dV^T += dO^T P; a dK wave computes S, dP and dS and accumulates
-// dK^T += Q^T dS. S is computed twice, but each wave holds one accumulator set,
-// so two waves fit on every SIMD.
+// (waves w and w + 4 share a SIMD). In step t a dV wave computes S and P of
+// query tile t, writes P to LDS and accumulates dV^T += dO^T P; the dK wave of
+// the same keys computes dP of tile t - 1, reads that tile's P, forms
+// dS = P (dP - D) and accumulates dK^T += Q^T dS. Each wave holds one
+// accumulator set and one set of key rows, so two waves fit on every SIMD, and
+// the two roles' MFMA and VALU work overlap within a step instead of waiting
+// for each other.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -88,12 +158,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const float* __restrict__ slopes, float c1, float scale) {
   constexpr int NT = 512, BK = 128, BQ = 32;
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
-  constexpr int RPITCH = D * 2 + 16;  // row-major Q / dO rows, bytes
-  constexpr int RBYTES = BQ * RPITCH;
+  using Tile = SwzTile<D>;             // Q / dO tiles: swizzled rows of 2 D bytes
+  constexpr int RBYTES = BQ * Tile::ROWB;
   constexpr int STAGE = 2 * RBYTES + 2 * BQ * 4;
   constexpr int CHUNKS = BQ * CPR;    // 16-byte chunks of Q (and of dO) per tile
   static_assert(CHUNKS <= NT, "one chunk per thread at most");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[3 * STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -116,6 +186,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   f32x16 cinit;
 #pragma unroll
   for (int r = 0; r < 16; ++r) cinit[r] = -c21 * float(8 * (r >> 2) + (r & 3));
+  // per-lane byte offsets of the swizzled tile reads
+  const int rb = Tile::row_base(lane), tb0 = Tile::tr_base(lane, 0), tb1 = Tile::tr_base(lane, 1);
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? k0 / BQ : 0;
@@ -123,14 +195,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // staging registers of one query tile (one chunk of Q and of dO per thread)
   u32x4 rq = {0u, 0u, 0u, 0u}, rdo = {0u, 0u, 0u, 0u};
   float rl = 0.0f, rd = 0.0f;
+  // chunk tid of a tile: global row q0 + tid / CPR, chunk tid % CPR, i.e. byte
+  // 16 tid past the tile's first row; rows past N read as zero
+  const __amdgpu_buffer_rsrc_t rsq = rows_rsrc<D>(q + base, N), rsdo = rows_rsrc<D>(dout + base, N);
+  const int sto = Tile::off(tid / CPR, tid % CPR);
   auto load_tile = [&](int qt) {
     const int q0 = qt * BQ;
-    const int row = tid / CPR, col = tid % CPR;
-    rq = u32x4{0u, 0u, 0u, 0u};
-    rdo = u32x4{0u, 0u, 0u, 0u};
-    if (tid < CHUNKS && q0 + row < N) {
-      rq = load16(q + base + (long long)(q0 + row) * D + col * 8);
-      rdo = load16(dout + base + (long long)(q0 + row) * D + col * 8);
+    if (tid < CHUNKS) {
+      const uint32_t vo = uint32_t(q0) * (D * 2) + uint32_t(tid) * 16u;
+      rq = bload16(rsq, vo);
+      rdo = bload16(rsdo, vo);
     }
     if (tid < BQ) {
       const bool ok = q0 + tid < N;
@@ -139,10 +213,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
   };
   auto store_tile = [&](unsigned char* st) {
-    const int row = tid / CPR, col = tid % CPR;
     if (tid < CHUNKS) {
-      *reinterpret_cast<u32x4*>(st + row * RPITCH + col * 16) = rq;
-      *reinterpret_cast<u32x4*>(st + RBYTES + row * RPITCH + col * 16) = rdo;
+      *reinterpret_cast<u32x4*>(st + sto) = rq;
+      *reinterpret_cast<u32x4*>(st + RBYTES + sto) = rdo;
     }
     if (tid < BQ) {
       float* sL = reinterpret_cast<float*>(st + 2 * RBYTES);
@@ -163,7 +236,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     f32x16 s = cinit;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + l32 * RPITCH + (16 * ks + 8 * hi) * 2);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + (rb ^ (32 * ks)));
       s = mfma32(a, kf[ks], s);
     }
     return s;
@@ -188,57 +261,80 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
   };
 
+  // P of a tile, computed by the dV wave of each key group and read by the dK
+  // wave of the same group one step later: per group and buffer 16 fp32 values
+  // per lane, quad c of lane l at 16 (64 c + l).
+  __shared__ __attribute__((aligned(16))) float sP[2][4][4][64][4];
+  // Step t: the dV waves take query tile t (S, P, dV), the dK waves tile t - 1
+  // (dP, dS = P (dP - D), dK) with the P the dV waves wrote in step t - 1.
+  // Tile t sits in stage t % 3; during step t the stage of tile t - 2 (free
+  // after the barrier that starts the step) receives tile t + 1.
+  auto stage_of = [&](int t) { return smem + ((t - qt0) % 3) * STAGE; };
   if (qt0 < nqt) {
     load_tile(qt0);
-    store_tile(smem);
+    store_tile(stage_of(qt0));
+    if (qt0 + 1 < nqt) load_tile(qt0 + 1);
   }
-  // Each role runs its own loop (a wave only ever runs one of them), so the
-  // two accumulator sets are never live together; both loops meet the same
-  // barriers.
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   if (role == 0) {
     bf16x8 kf[KS];
     load_frags(k, kf);
-    int stage = 0;
-    for (int qt = qt0; qt < nqt; ++qt, stage ^= 1) {
+    for (int t = qt0; t <= nqt; ++t) {
       __syncthreads();
-      if (qt + 1 < nqt) load_tile(qt + 1);
-      const unsigned char* st = smem + stage * STAGE;
-      const int q0 = qt * BQ;
+      if (t + 1 < nqt) {
+        store_tile(stage_of(t + 1));
+        if (t + 2 < nqt) load_tile(t + 2);
+      }
+      if (t == nqt) break;
+      const unsigned char* st = stage_of(t);
+      const int q0 = t * BQ;
       if (!CAUSAL || q0 + BQ - 1 >= kw0) {
         f32x16 p = scores(st, kf);
         probs(p, reinterpret_cast<const float*>(st + 2 * RBYTES), q0);
+        float4* const wp = reinterpret_cast<float4*>(&sP[(t - qt0) & 1][wave & 3][0][0][0]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wp[64 * c + lane] = float4{p[4 * c], p[4 * c + 1], p[4 * c + 2], p[4 * c + 3]};
         const u32x4 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          acc[db] = mfma32(read_tr(st + RBYTES, RPITCH, 0, 32 * db, lane), __builtin_bit_cast(bf16x8, pb0), acc[db]);
-          acc[db] = mfma32(read_tr(st + RBYTES, RPITCH, 16, 32 * db, lane), __builtin_bit_cast(bf16x8, pb1), acc[db]);
+          acc[db] = mfma32(read_tr<D>(st + RBYTES, tb0, tb1, 0, 32 * db), __builtin_bit_cast(bf16x8, pb0), acc[db]);
+          acc[db] = mfma32(read_tr<D>(st + RBYTES, tb0, tb1, 16, 32 * db), __builtin_bit_cast(bf16x8, pb1), acc[db]);
         }
       }
-      if (qt + 1 < nqt) store_tile(smem + (stage ^ 1) * STAGE);
     }
   } else {
-    bf16x8 kf[KS], vf[KS];
-    load_frags(k, kf);
+    bf16x8 vf[KS];
     load_frags(v, vf);
-    int stage = 0;
-    for (int qt = qt0; qt < nqt; ++qt, stage ^= 1) {
+    for (int t = qt0; t <= nqt; ++t) {
       __syncthreads();
-      if (qt + 1 < nqt) load_tile(qt + 1);
-      const unsigned char* st = smem + stage * STAGE;
+      if (t + 1 < nqt) {
+        store_tile(stage_of(t + 1));
+        if (t + 2 < nqt) load_tile(t + 2);
+      }
+      if (t == qt0) continue;
+      const int u = t - 1;  // this wave's tile
+      const unsigned char* st = stage_of(u);
       const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
-      const int q0 = qt * BQ;
+      const int q0 = u * BQ;
       if (!CAUSAL || q0 + BQ - 1 >= kw0) {
-        f32x16 p = scores(st, kf);
         f32x16 dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + RBYTES + l32 * RPITCH + (16 * ks + 8 * hi) * 2);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + RBYTES + (rb ^ (32 * ks)));
           dp = mfma32(a, vf[ks], dp);
         }
-        probs(p, sL, q0);
+        const float4* const rp = reinterpret_cast<const float4*>(&sP[(u - qt0) & 1][wave & 3][0][0][0]);
+        f32x16 p;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float4 x = rp[64 * c + lane];
+          p[4 * c] = x.x;
+          p[4 * c + 1] = x.y;
+          p[4 * c + 2] = x.z;
+          p[4 * c + 3] = x.w;
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4 Dv = *reinterpret_cast<const f32x4*>(sL + BQ + 8 * g + 4 * hi);
@@ -248,11 +344,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         const u32x4 sb0 = pack8(p, 0), sb1 = pack8(p, 8);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          acc[db] = mfma32(read_tr(st, RPITCH, 0, 32 * db, lane), __builtin_bit_cast(bf16x8, sb0), acc[db]);
-          acc[db] = mfma32(read_tr(st, RPITCH, 16, 32 * db, lane), __builtin_bit_cast(bf16x8, sb1), acc[db]);
+          acc[db] = mfma32(read_tr<D>(st, tb0, tb1, 0, 32 * db), __builtin_bit_cast(bf16x8, sb0), acc[db]);
+          acc[db] = mfma32(read_tr<D>(st, tb0, tb1, 16, 32 * db), __builtin_bit_cast(bf16x8, sb1), acc[db]);
         }
       }
-      if (qt + 1 < nqt) store_tile(smem + (stage ^ 1) * STAGE);
     }
   }
 
@@ -282,8 +377,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     float c1, float scale) {
   constexpr int NT = 256, BM = 128, BN = 64;
   constexpr int KS = D / 16, KB = BN / 32, DB = D / 32, PS = BN / 16, CPR = D / 8;
-  constexpr int KPITCH = D * 2 + 16;   // K and V rows, bytes
-  constexpr int KBYTES = BN * KPITCH;
+  using Tile = SwzTile<D>;              // K and V tiles: swizzled rows of 2 D bytes
+  constexpr int KBYTES = BN * Tile::ROWB;
   constexpr int STAGE = 2 * KBYTES;
   constexpr int LOADS = BN * CPR / NT;
   static_assert(LOADS * NT == BN * CPR, "tile must split evenly");
@@ -321,6 +416,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   f32x16 cinit;
 #pragma unroll
   for (int r = 0; r < 16; ++r) cinit[r] = c21 * float(8 * (r >> 2) + (r & 3));
+  const int rb = Tile::row_base(lane), tb0 = Tile::tr_base(lane, 0), tb1 = Tile::tr_base(lane, 1);
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
@@ -329,24 +425,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int ntiles = (kend + BN - 1) / BN;
 
   u32x4 rk[LOADS], rv[LOADS];
+  // chunk tid + NT r of a tile: byte 16 (tid + NT r) past its first row; rows
+  // past N read as zero. In LDS it sits NT / CPR rows (a multiple of 16, so the
+  // same swizzle) below chunk tid.
+  const __amdgpu_buffer_rsrc_t rsk = rows_rsrc<D>(k + base, N), rsv = rows_rsrc<D>(v + base, N);
+  const int sto = Tile::off(tid / CPR, tid % CPR);
+  static_assert((NT / CPR) % 16 == 0, "row step keeps the swizzle");
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
-      const int c = tid + NT * r, row = c / CPR, col = c % CPR;
-      rk[r] = u32x4{0u, 0u, 0u, 0u};
-      rv[r] = u32x4{0u, 0u, 0u, 0u};
-      if (j0 + row < N) {
-        rk[r] = load16(k + base + (long long)(j0 + row) * D + col * 8);
-        rv[r] = load16(v + base + (long long)(j0 + row) * D + col * 8);
-      }
+      const uint32_t vo = uint32_t(j0) * (D * 2) + uint32_t(tid + NT * r) * 16u;
+      rk[r] = bload16(rsk, vo);
+      rv[r] = bload16(rsv, vo);
     }
   };
   auto store_tile = [&](unsigned char* st) {
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
-      const int c = tid + NT * r, row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(st + row * KPITCH + col * 16) = rk[r];
-      *reinterpret_cast<u32x4*>(st + KBYTES + row * KPITCH + col * 16) = rv[r];
+      *reinterpret_cast<u32x4*>(st + sto + r * (NT / CPR) * Tile::ROWB) = rk[r];
+      *reinterpret_cast<u32x4*>(st + KBYTES + sto + r * (NT / CPR) * Tile::ROWB) = rv[r];
     }
   };
 
@@ -374,9 +471,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         f32x16 s = cinit, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + 32 * kb * Tile::ROWB + (rb ^ (32 * ks)));
           s = mfma32(a, qf[ks], s);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(sV + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(sV + 32 * kb * Tile::ROWB + (rb ^ (32 * ks)));
           dp = mfma32(b, of[ks], dp);
         }
 #pragma unroll
@@ -404,7 +501,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int ps = 0; ps < PS; ++ps)
-          acc[db] = mfma32(read_tr(sK, KPITCH, 16 * ps, 32 * db, lane), __builtin_bit_cast(bf16x8, pf[ps]), acc[db]);
+          acc[db] = mfma32(read_tr<D>(sK, tb0, tb1, 16 * ps, 32 * db), __builtin_bit_cast(bf16x8, pf[ps]), acc[db]);
       }
     }
     if (tile > 0) store_tile(smem + (stage ^ 1) * STAGE);

@@ -42,23 +42,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// MFMA A operand (rows = 32 d values, k = 16 rows of a row-major LDS tile)
-// read transposed with ds_read_b64_tr_b16: within each 16-lane group, lanes
-// 4e .. 4e + 3 point at 8-byte pieces of tile row e and lane j receives
-// column j of those 4 rows. Lane l gets d = dcol + l % 32 and tile rows
-// r16 + {0..3, 8..11} (l < 32) or r16 + {4..7, 12..15} (l >= 32): the row
-// order of the 32x32 accumulator layout, so an accumulator used as the B
-// operand pairs each of its rows with the matching tile row.
-__device__ __forceinline__ bf16x8 read_tr(const unsigned char* tile, int pitch, int r16, int dcol, int lane) {
-  const int j = lane & 15, g = (lane >> 4) & 1, hi = lane >> 5;
-  const int row = r16 + 4 * hi + (j >> 2);
-  const int off = row * pitch + (dcol + 16 * g + 4 * (j & 3)) * 2;
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off + 8 * pitch));
-  const short v8 __attribute__((ext_vector_type(8))) = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, v8);
-}
-
 // Workgroup w -> ((b, h) pair, block rank) for nbh pairs of nblk blocks each.
 // Workgroups are dealt round-robin to the 8 XCDs (w % 8). With nbh a multiple
 // of 8 every XCD gets whole (b, h) pairs, so a head's K and V stay in that
