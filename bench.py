@@ -136,7 +136,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "copy", "bwd"], default=None)
+    ap.add_argument("--only", choices=["fwd", "fwd16k", "decode", "copy", "bwd"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -289,12 +289,13 @@ def next_forms(alibi, q, k, v, s, fw):
 def run_only(args, alibi, W, fw, dw, dev):
     """One kernel, W + K launches, HIP-event timed; for counter runs."""
     import torch
-    if args.only == "fwd":
-        q, k, v = (x.to(dev) for x in W.gaussian_qkv_bf16(fw.shape, seed=fw.seed))
+    if args.only in ("fwd", "fwd16k"):
+        wl = fw if args.only == "fwd" else W.FWD_B1_H16_N16384_D128
+        q, k, v = (x.to(dev) for x in W.gaussian_qkv_bf16(wl.shape, seed=wl.seed))
         out = torch.empty_like(q)
-        s = alibi.slopes(fw.H).to(dev)
+        s = alibi.slopes(wl.H).to(dev)
         fn = lambda: alibi.attn_fwd(q, k, v, s, causal=True, out=out)
-        work, unit = fwd_flops(fw.B, fw.H, fw.N, fw.d), "flop"
+        work, unit = fwd_flops(wl.B, wl.H, wl.N, wl.d), "flop"
     elif args.only == "decode":
         kc = W.device_gaussian_bf16((dw.B, dw.H, dw.L, dw.d), seed=dw.seed)
         vc = W.device_gaussian_bf16((dw.B, dw.H, dw.L, dw.d), seed=dw.seed + 1)
