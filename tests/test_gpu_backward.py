@@ -49,6 +49,9 @@ def _inputs(shape, seed):
 @pytest.mark.parametrize("B,H,N,d,causal", [
     (1, 2, 33, 64, True), (1, 2, 100, 64, False), (2, 3, 300, 128, True),
     (1, 4, 1000, 64, True), (1, 2, 513, 128, False), (2, 2, 200, 128, True),
+    # a key block with a single query tile (N = 129: keys 128.. see one 32-row tile),
+    # shorter than one tile, a single token, and a non-causal multi-tile d = 128 case
+    (1, 2, 129, 128, True), (1, 3, 16, 64, True), (1, 2, 1, 128, True), (2, 2, 160, 128, False),
 ])
 def test_backward_small(alibi, B, H, N, d, causal):
     q, k, v, do = _inputs((B, H, N, d), 31)
