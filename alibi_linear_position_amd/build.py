@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libalibi.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "fwd_generic.hip", "fwd_mfma.hip", "decode.hip", "knorm.hip", "bwd.hip"]
+SOURCES = ["api.cpp", "fwd_generic.hip", "fwd_mfma.hip", "decode.hip", "knorm.hip", "bwd.hip",
+           "stream_read.hip"]
 
 
 def hipcc() -> str:

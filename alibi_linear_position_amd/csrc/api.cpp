@@ -264,6 +264,15 @@ int alibi_debug_schedule(int w, int nbh, int nblk, int* out2) {
   return ALIBI_OK;
 }
 
+int alibi_debug_stream_read(const void* buf, long long bytes, unsigned* sink, int workgroups,
+                            hipStream_t stream) {
+  if (buf == nullptr || sink == nullptr || bytes < 16 || bytes % 16 != 0 || workgroups < 1 ||
+      workgroups > 65536 || (reinterpret_cast<uintptr_t>(buf) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+    return ALIBI_EINVAL;
+  return hip_status(alibi::launch_stream_read(buf, bytes, sink, workgroups, stream));
+}
+
 int alibi_debug_fwd_waves(int nw) {
   if (nw != 0 && nw != 4 && nw != 8) return ALIBI_EINVAL;
   alibi::set_fwd_waves(nw);

@@ -50,7 +50,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Few pairs in flight keep the XCD's L2 on their K and V, and rank order keeps
 // heavy blocks from starting late. Otherwise ranks go in order over all pairs.
 // Host and device: the host side is checked to be a bijection.
-constexpr int kSchedGroup = 2;
+constexpr int kSchedGroup = 4;
 struct WgBlock {
   int bh;
   int rank;

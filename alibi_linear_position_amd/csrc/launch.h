@@ -67,6 +67,8 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hi
 
 // Largest key norm of each (b, h) of k (B, H, N, d) bf16, d in {64, 128}, as P
 // partial maxima: out[(b H + h) P + p].
+// Streaming read of `bytes` (a multiple of 16) from buf, one XOR word per workgroup to sink.
+hipError_t launch_stream_read(const void* buf, long long bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 hipError_t launch_knorm_max(const void* k, float* out, int B, int H, int N, int d, int P,
                             hipStream_t stream);
 

@@ -193,6 +193,7 @@ def main():
     tflops = flops / t_fwd / 1e12
     gbs = nbytes / t_dec / 1e9
     assert torch.isfinite(out.float()).all() and torch.isfinite(od.float()).all()
+    read_gbs = read_ceiling(alibi, (kc, vc), dev)
 
     res = {
         "metric": "causal ALiBi attn fwd TFLOP/s (bf16) + decode HBM GB/s, 1xMI355X",
@@ -222,7 +223,11 @@ def main():
                                 "traffic": traffic_bytes("decode_split_B32_H32_L32768_d128.md",
                                                          ["decode.hip", "device_common.h"]),
                                 "kernel": "decode_split_kernel<16>", "ms_per_launch": round(t_dec * 1e3, 4),
-                                "per_launch": f"{nbytes:.4e} B"}},
+                                "per_launch": f"{nbytes:.4e} B",
+                                "read_ceiling": {"value": round(read_gbs, 1), "unit": "GB/s",
+                                                 "kernel": "stream_read_kernel",
+                                                 "note": "plain streaming read of the same K and V caches; "
+                                                         "context, not the peak"}}},
         "cpu_baseline": None,
     }
     res["next"] = next_forms(alibi, qg, kg, vg, s_f, fw)
@@ -284,6 +289,33 @@ def next_forms(alibi, q, k, v, s, fw):
     res["chunked_prefill_512_of_4096"] = {"value": round(4.0 * d * B * H * vis / ms / 1e9, 1),
                                           "unit": "TFLOP/s", "ms": round(ms, 4)}
     return res
+
+
+def read_ceiling(alibi, tensors, dev, workgroups=4096, warmup=2, steps=5):
+    """GB/s of a plain streaming read (16-byte loads, every byte once) over the
+    given device tensors: the practical read ceiling beside the decode's rate."""
+    import torch
+    lib = alibi.load_library()
+    sink = torch.empty(workgroups, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    nbytes = sum(t.numel() * t.element_size() for t in tensors)
+
+    def once():
+        for t in tensors:
+            rc = lib.alibi_debug_stream_read(t.data_ptr(), t.numel() * t.element_size(), sink.data_ptr(),
+                                             workgroups, st)
+            assert rc == 0, rc
+
+    for _ in range(warmup):
+        once()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        once()
+    e1.record()
+    torch.cuda.synchronize()
+    return nbytes * steps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
 def run_only(args, alibi, W, fw, dw, dev):

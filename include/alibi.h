@@ -253,6 +253,19 @@ int alibi_debug_schedule(int w, int nbh, int nblk, int* out2);
  */
 int alibi_debug_fwd_waves(int nw);
 
+/*
+ * MEASUREMENT ONLY: a plain streaming read of `bytes` bytes of device memory
+ * at `buf` (16-byte aligned, bytes a positive multiple of 16), the practical
+ * HBM read ceiling against which the decode's bandwidth is read. Each of
+ * `workgroups` (1 .. 65536) workgroups of 256 threads writes the XOR of the
+ * 32-bit words it read to sink[workgroup] (device memory, 4-byte aligned, room
+ * for `workgroups` words), so the XOR of the sink equals the XOR of the buffer.
+ * Asynchronous on `stream`. ALIBI_EINVAL for bad arguments (checked before
+ * anything is enqueued).
+ */
+int alibi_debug_stream_read(const void* buf, long long bytes, unsigned* sink, int workgroups,
+                            hipStream_t stream);
+
 /* Static, never-NULL description of a status code. */
 const char* alibi_status_string(int status);
 

@@ -220,3 +220,19 @@ def test_fwd_waves_override_validation(lib):
     for nw in (-1, 1, 2, 6, 16):
         assert lib.alibi_debug_fwd_waves(nw) == -1
     assert lib.alibi_debug_fwd_waves(0) == 0
+
+
+def test_stream_read_validation(lib):
+    # host-side checks only: every bad argument is refused before any launch
+    P = ctypes.c_void_p
+    f = lib.alibi_debug_stream_read
+    f.argtypes = [P, ctypes.c_longlong, P, ctypes.c_int, P]
+    ok_buf, ok_sink = P(4096), P(8192)
+    assert f(None, 64, ok_sink, 4, None) == -1
+    assert f(ok_buf, 64, None, 4, None) == -1
+    assert f(P(4100), 64, ok_sink, 4, None) == -1       # buffer not 16-byte aligned
+    assert f(ok_buf, 0, ok_sink, 4, None) == -1
+    assert f(ok_buf, 40, ok_sink, 4, None) == -1        # not a multiple of 16
+    assert f(ok_buf, 64, P(8194), 4, None) == -1        # sink not 4-byte aligned
+    assert f(ok_buf, 64, ok_sink, 0, None) == -1
+    assert f(ok_buf, 64, ok_sink, 65537, None) == -1
