@@ -136,7 +136,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd16k", "decode", "copy", "bwd"], default=None)
+    ap.add_argument("--only", choices=["fwd", "fwd16k", "decode", "copy", "bwd", "oracle"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -318,9 +318,83 @@ def read_ceiling(alibi, tensors, dev, workgroups=4096, warmup=2, steps=5):
     return nbytes * steps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def oracle_timing(W, dw, dev):
+    """The fp64 oracle timed per configuration on this host's cores (a reported
+    baseline, not the target): the tiny fp32 case and the two d = 64 forwards
+    (also single-threaded), the 16384-token forward and the decode (host copies
+    excluded), each whole."""
+    import numpy as np
+    import torch
+    import oracle
+    from threadpoolctl import threadpool_limits
+    threads = len(os.sched_getaffinity(0))
+    model = "unknown"
+    with open("/proc/cpuinfo") as f:
+        for line in f:
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    res = {"only": "oracle", "cpu": model, "threads": threads, "cases": []}
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    def record(name, seconds, work, unit, nthreads, note):
+        rate = work / seconds / (1e9 if unit == "GB/s" else 1e9)
+        res["cases"].append({"case": name, "seconds": round(seconds, 4), "rate": round(rate, 4), "unit": unit,
+                             "threads": nthreads, "note": note})
+        print(f"[oracle] {name}: {seconds:.3f} s, {rate:.4g} {unit}, {nthreads} threads", flush=True)
+
+    q, k, v = W.tiny_example_qkv()
+    s4 = oracle.slopes_ref(4)
+    for nt in (threads, 1):
+        with threadpool_limits(nt):
+            t = timed(lambda: oracle.attn_ref(q[None], k[None], v[None], s4, causal=True), 3)
+        record("tiny fp32 B1 H4 N8 d16", t, fwd_flops(1, 4, 8, 16), "GFLOP/s", nt, "median of 3")
+    for wl, reps1 in ((W.FWD_B8_H8_N1024_D64, 3), (W.FWD_B4_H12_N2048_D64, 1)):
+        qq, kk, vv = (x.to(torch.float64).numpy() for x in W.gaussian_qkv_bf16(wl.shape, seed=wl.seed))
+        sl = oracle.slopes_ref(wl.H)
+        for nt, reps in ((threads, 3), (1, reps1)):
+            with threadpool_limits(nt):
+                t = timed(lambda: oracle.attn_ref(qq, kk, vv, sl, causal=True), reps)
+            record(wl.name, t, fwd_flops(wl.B, wl.H, wl.N, wl.d), "GFLOP/s", nt, f"median of {reps}")
+    wl = W.FWD_B1_H16_N16384_D128
+    qq, kk, vv = (x[0].to(torch.float64).numpy() for x in W.gaussian_qkv_bf16(wl.shape, seed=wl.seed))
+    sl = oracle.slopes_ref(wl.H)
+    total = 0.0
+    for h in range(wl.H):  # one head at a time: each materialises 16384 x 16384 fp64 matrices
+        t0 = time.perf_counter()
+        oracle.attn_head_ref(qq[h], kk[h], vv[h], float(sl[h]), causal=True)
+        total += time.perf_counter() - t0
+        print(f"[oracle] {wl.name} head {h}: {time.perf_counter() - t0:.2f} s", flush=True)
+    record(wl.name, total, fwd_flops(wl.B, wl.H, wl.N, wl.d), "GFLOP/s", threads, "1 run")
+    kc = W.device_gaussian_bf16((dw.B, dw.H, dw.L, dw.d), seed=dw.seed)
+    vc = W.device_gaussian_bf16((dw.B, dw.H, dw.L, dw.d), seed=dw.seed + 1)
+    qd = W.device_gaussian_bf16((dw.B, dw.H, dw.d), seed=dw.seed + 2)
+    sd = oracle.slopes_ref(dw.H)
+    total = 0.0
+    for b in range(dw.B):
+        for h in range(dw.H):
+            qh, kh, vh = qd[b:b + 1, h:h + 1].cpu(), kc[b:b + 1, h:h + 1].cpu(), vc[b:b + 1, h:h + 1].cpu()
+            t0 = time.perf_counter()
+            oracle.decode_ref(qh, kh, vh, sd[h:h + 1])
+            total += time.perf_counter() - t0
+        print(f"[oracle] {dw.name} batch {b} done, {total:.1f} s so far", flush=True)
+    record(dw.name, total, decode_bytes(dw.B, dw.H, dw.L, dw.d), "GB/s", threads,
+           "1 run, host copies excluded")
+    print(json.dumps(res), flush=True)
+
+
 def run_only(args, alibi, W, fw, dw, dev):
     """One kernel, W + K launches, HIP-event timed; for counter runs."""
     import torch
+    if args.only == "oracle":
+        return oracle_timing(W, dw, dev)
     if args.only in ("fwd", "fwd16k"):
         wl = fw if args.only == "fwd" else W.FWD_B1_H16_N16384_D128
         q, k, v = (x.to(dev) for x in W.gaussian_qkv_bf16(wl.shape, seed=wl.seed))
