@@ -31,6 +31,7 @@
 #include "launch.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace alibi {
 
@@ -451,19 +452,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     load_tile((ntiles - 1) * BN);
     store_tile(smem);
   }
+  // Tiles wholly at or before the block's first query (and below N) need no
+  // mask for any wave; their bias is the causal one in both modes. The others
+  // (the diagonal, and without the causal mask the tiles after the queries)
+  // are visited first and take the per-score mask. Two loops, so the open
+  // tiles carry no mask arithmetic at all.
   int stage = 0;
-  for (int tile = ntiles - 1; tile >= 0; --tile, stage ^= 1) {
+  auto step = [&](int tile, auto open_tag) {
+    constexpr bool OPEN = decltype(open_tag)::value;
     const int j0 = tile * BN;
     __syncthreads();
     if (tile > 0) load_tile(j0 - BN);
     const unsigned char* st = smem + stage * STAGE;
     const unsigned char* sK = st;
     const unsigned char* sV = st + KBYTES;
-    const bool active = qw0 < N && (!CAUSAL || j0 <= qw_last);
+    const bool active = qw0 < N && (OPEN || !CAUSAL || j0 <= qw_last);
     if (active) {
       // ---- per 32-key block: S^T = K Q^T, dP^T = V dO^T (lane = query), then
       // P^T = exp2(t - lse2) and dS^T = P^T (dP^T - D) packed to bf16 ----
-      const bool full = CAUSAL && j0 + BN - 1 <= qw0 && j0 + BN <= N;
+      const bool full = OPEN || (CAUSAL && j0 + BN - 1 <= qw0 && j0 + BN <= N);
       const float bt0 = c2 * float(j0 + 4 * hi - i) - L;
       u32x4 pf[PS];
 #pragma unroll
@@ -482,9 +489,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * half + e;
-            const int jj = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
             float t = fmaf(s[r], c1, bt0 + 32.0f * kb * c2);
-            if (!full) {
+            if (!OPEN && !full) {
+              const int jj = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
               if (!CAUSAL && jj > i) t -= 2.0f * c2 * float(jj - i);
               if (jj >= N || (CAUSAL && jj > i)) t = -__builtin_huge_valf();
             }
@@ -505,7 +512,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       }
     }
     if (tile > 0) store_tile(smem + (stage ^ 1) * STAGE);
-  }
+    stage ^= 1;
+  };
+  const int x_open = q0 + 1;  // keys [0, x_open) are at or before every query of the block
+  const int t_open = x_open < BN ? -1 : min(min(x_open / BN - 1, N / BN - 1), ntiles - 1);
+  int tile = ntiles - 1;
+  for (; tile > t_open; --tile) step(tile, std::false_type{});
+  for (; tile >= 0; --tile) step(tile, std::true_type{});
 
   if (i < N) {
 #pragma unroll
