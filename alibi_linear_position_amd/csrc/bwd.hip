@@ -242,9 +242,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
     return s;
   };
-  auto probs = [&](f32x16& s, const float* sL, int q0) {
+  auto probs = [&](f32x16& s, const float* sL, int q0, auto open_tag) {
+    constexpr bool OPEN = decltype(open_tag)::value;  // no query of the tile precedes a key of the block
     const float bj = c2 * float(j - q0 - 4 * hi);  // t = s c1 + bj on the causal side
-    const bool full = CAUSAL && q0 >= kw0 + 31;    // every query of the tile sees every key of the wave
+    const bool full = OPEN || (CAUSAL && q0 >= kw0 + 31);  // every query of the tile sees every key of the wave
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 L = *reinterpret_cast<const f32x4*>(sL + 8 * g + 4 * hi);
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         const int r = 4 * g + e;
         const int i = q0 + 8 * g + 4 * hi + e;
         float t = fmaf(s[r], c1, bj);
-        if (!full) {
+        if (!OPEN && !full) {
           if (!CAUSAL && j > i) t -= 2.0f * c2 * float(j - i);  // symmetric bias -m |i - j|
           if (CAUSAL && j > i) t = -__builtin_huge_valf();
         }
@@ -282,18 +283,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   if (role == 0) {
     bf16x8 kf[KS];
     load_frags(k, kf);
-    for (int t = qt0; t <= nqt; ++t) {
+    auto vstep = [&](int t, auto open_tag) {
+      constexpr bool OPEN = decltype(open_tag)::value;
       __syncthreads();
       if (t + 1 < nqt) {
         store_tile(stage_of(t + 1));
         if (t + 2 < nqt) load_tile(t + 2);
       }
-      if (t == nqt) break;
+      if (t == nqt) return;
       const unsigned char* st = stage_of(t);
       const int q0 = t * BQ;
-      if (!CAUSAL || q0 + BQ - 1 >= kw0) {
+      if (OPEN || !CAUSAL || q0 + BQ - 1 >= kw0) {
         f32x16 p = scores(st, kf);
-        probs(p, reinterpret_cast<const float*>(st + 2 * RBYTES), q0);
+        probs(p, reinterpret_cast<const float*>(st + 2 * RBYTES), q0, open_tag);
         float4* const wp = reinterpret_cast<float4*>(&sP[(t - qt0) & 1][wave & 3][0][0][0]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) wp[64 * c + lane] = float4{p[4 * c], p[4 * c + 1], p[4 * c + 2], p[4 * c + 3]};
@@ -304,7 +306,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           acc[db] = mfma32(read_tr<D>(st + RBYTES, tb0, tb1, 16, 32 * db), __builtin_bit_cast(bf16x8, pb1), acc[db]);
         }
       }
-    }
+    };
+    // Query tiles that start at or after the block's last key see every key of
+    // the block: no mask (two loops, so those tiles carry no mask arithmetic).
+    const int t_open = (k0 + BK - 1 + BQ - 1) / BQ;
+    int t = qt0;
+    for (; t <= nqt && t < t_open; ++t) vstep(t, std::false_type{});
+    for (; t <= nqt; ++t) vstep(t, std::true_type{});
   } else {
     bf16x8 vf[KS];
     load_frags(v, vf);
