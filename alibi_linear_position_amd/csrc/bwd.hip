@@ -280,16 +280,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  // Staging of step t, done after the step's MFMAs are issued so that the
+  // wait for the loads and the LDS writes overlap them: tile t + 1 (loaded in
+  // step t - 1) goes to its stage, whose last readers finished before the
+  // barrier that started step t, and the loads of tile t + 2 are issued.
+  auto stage_next = [&](int t) {
+    if (t + 1 < nqt) {
+      store_tile(stage_of(t + 1));
+      if (t + 2 < nqt) load_tile(t + 2);
+    }
+  };
   if (role == 0) {
     bf16x8 kf[KS];
     load_frags(k, kf);
     auto vstep = [&](int t, auto open_tag) {
       constexpr bool OPEN = decltype(open_tag)::value;
       __syncthreads();
-      if (t + 1 < nqt) {
-        store_tile(stage_of(t + 1));
-        if (t + 2 < nqt) load_tile(t + 2);
-      }
       if (t == nqt) return;
       const unsigned char* st = stage_of(t);
       const int q0 = t * BQ;
@@ -306,6 +312,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           acc[db] = mfma32(read_tr<D>(st + RBYTES, tb0, tb1, 16, 32 * db), __builtin_bit_cast(bf16x8, pb1), acc[db]);
         }
       }
+      stage_next(t);
     };
     // Query tiles that start at or after the block's last key see every key of
     // the block: no mask (two loops, so those tiles carry no mask arithmetic).
@@ -318,11 +325,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     load_frags(v, vf);
     for (int t = qt0; t <= nqt; ++t) {
       __syncthreads();
-      if (t + 1 < nqt) {
-        store_tile(stage_of(t + 1));
-        if (t + 2 < nqt) load_tile(t + 2);
+      if (t == qt0) {
+        stage_next(t);
+        continue;
       }
-      if (t == qt0) continue;
       const int u = t - 1;  // this wave's tile
       const unsigned char* st = stage_of(u);
       const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
@@ -357,6 +363,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           acc[db] = mfma32(read_tr<D>(st, tb0, tb1, 16, 32 * db), __builtin_bit_cast(bf16x8, sb1), acc[db]);
         }
       }
+      stage_next(t);
     }
   }
 
