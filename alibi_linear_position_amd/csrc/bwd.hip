@@ -108,6 +108,26 @@ __device__ __forceinline__ bf16x8 read_tr(const unsigned char* tile, int tb0, in
   return __builtin_bit_cast(bf16x8, v8);
 }
 
+// NF MFMAs whose A operands come from LDS: fragment n is read DEPTH MFMAs
+// ahead of its use and the order is pinned (sched_barrier), so several reads
+// stay in flight; left to itself the scheduler keeps one or two, and a wave
+// whose SIMD partner is not issuing MFMAs then waits on LDS latency before
+// most of them. frag(n) reads fragment n; op(n, a) issues MFMA n.
+template <int NF, int DEPTH, typename Frag, typename Op>
+__device__ __forceinline__ void lds_mfma_ring(Frag&& frag, Op&& op) {
+  bf16x8 ring[DEPTH];
+#pragma unroll
+  for (int n = 0; n < DEPTH; ++n) ring[n] = frag(n);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < NF; ++n) {
+    const bf16x8 a = ring[n % DEPTH];
+    if (n + DEPTH < NF) ring[n % DEPTH] = frag(n + DEPTH);
+    op(n, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Pack 8 fp32 values (registers base .. base + 7 of an accumulator) to bf16.
 __device__ __forceinline__ u32x4 pack8(const f32x16& x, int base) {
   u32x4 r;
@@ -235,11 +255,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // S = Q K^T (rows = queries, lane = key) and P = exp2(t - lse2) of one tile
   auto scores = [&](const unsigned char* sQ, const bf16x8 (&kf)[KS]) {
     f32x16 s = cinit;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + (rb ^ (32 * ks)));
-      s = mfma32(a, kf[ks], s);
-    }
+    lds_mfma_ring<KS, 4>([&](int ks) { return *reinterpret_cast<const bf16x8*>(sQ + (rb ^ (32 * ks))); },
+                         [&](int ks, const bf16x8& a) { s = mfma32(a, kf[ks], s); });
     return s;
   };
   auto probs = [&](f32x16& s, const float* sL, int q0, auto open_tag) {
@@ -305,12 +322,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         float4* const wp = reinterpret_cast<float4*>(&sP[(t - qt0) & 1][wave & 3][0][0][0]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) wp[64 * c + lane] = float4{p[4 * c], p[4 * c + 1], p[4 * c + 2], p[4 * c + 3]};
-        const u32x4 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          acc[db] = mfma32(read_tr<D>(st + RBYTES, tb0, tb1, 0, 32 * db), __builtin_bit_cast(bf16x8, pb0), acc[db]);
-          acc[db] = mfma32(read_tr<D>(st + RBYTES, tb0, tb1, 16, 32 * db), __builtin_bit_cast(bf16x8, pb1), acc[db]);
-        }
+        const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, pack8(p, 0)), __builtin_bit_cast(bf16x8, pack8(p, 8))};
+        lds_mfma_ring<2 * DB, 4>(
+            [&](int n) { return read_tr<D>(st + RBYTES, tb0, tb1, 16 * (n & 1), 32 * (n >> 1)); },
+            [&](int n, const bf16x8& a) { acc[n >> 1] = mfma32(a, pb[n & 1], acc[n >> 1]); });
       }
       stage_next(t);
     };
@@ -335,11 +350,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const int q0 = u * BQ;
       if (!CAUSAL || q0 + BQ - 1 >= kw0) {
         f32x16 dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + RBYTES + (rb ^ (32 * ks)));
-          dp = mfma32(a, vf[ks], dp);
-        }
+        lds_mfma_ring<KS, 4>(
+            [&](int ks) { return *reinterpret_cast<const bf16x8*>(st + RBYTES + (rb ^ (32 * ks))); },
+            [&](int ks, const bf16x8& a) { dp = mfma32(a, vf[ks], dp); });
         const float4* const rp = reinterpret_cast<const float4*>(&sP[(u - qt0) & 1][wave & 3][0][0][0]);
         f32x16 p;
 #pragma unroll
@@ -356,12 +369,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) p[4 * g + e] *= dp[4 * g + e] - Dv[e];  // dS = P (dP - D)
         }
-        const u32x4 sb0 = pack8(p, 0), sb1 = pack8(p, 8);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          acc[db] = mfma32(read_tr<D>(st, tb0, tb1, 0, 32 * db), __builtin_bit_cast(bf16x8, sb0), acc[db]);
-          acc[db] = mfma32(read_tr<D>(st, tb0, tb1, 16, 32 * db), __builtin_bit_cast(bf16x8, sb1), acc[db]);
-        }
+        const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, pack8(p, 0)), __builtin_bit_cast(bf16x8, pack8(p, 8))};
+        lds_mfma_ring<2 * DB, 4>(
+            [&](int n) { return read_tr<D>(st, tb0, tb1, 16 * (n & 1), 32 * (n >> 1)); },
+            [&](int n, const bf16x8& a) { acc[n >> 1] = mfma32(a, sb[n & 1], acc[n >> 1]); });
       }
       stage_next(t);
     }
