@@ -108,26 +108,6 @@ __device__ __forceinline__ bf16x8 read_tr(const unsigned char* tile, int tb0, in
   return __builtin_bit_cast(bf16x8, v8);
 }
 
-// NF MFMAs whose A operands come from LDS: fragment n is read DEPTH MFMAs
-// ahead of its use and the order is pinned (sched_barrier), so several reads
-// stay in flight; left to itself the scheduler keeps one or two, and a wave
-// whose SIMD partner is not issuing MFMAs then waits on LDS latency before
-// most of them. frag(n) reads fragment n; op(n, a) issues MFMA n.
-template <int NF, int DEPTH, typename Frag, typename Op>
-__device__ __forceinline__ void lds_mfma_ring(Frag&& frag, Op&& op) {
-  bf16x8 ring[DEPTH];
-#pragma unroll
-  for (int n = 0; n < DEPTH; ++n) ring[n] = frag(n);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int n = 0; n < NF; ++n) {
-    const bf16x8 a = ring[n % DEPTH];
-    if (n + DEPTH < NF) ring[n % DEPTH] = frag(n + DEPTH);
-    op(n, a);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 // Pack 8 fp32 values (registers base .. base + 7 of an accumulator) to bf16.
 __device__ __forceinline__ u32x4 pack8(const f32x16& x, int base) {
   u32x4 r;

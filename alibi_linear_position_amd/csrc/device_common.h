@@ -39,6 +39,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// NF MFMAs whose A operands come from LDS: fragment n is read DEPTH MFMAs
+// ahead of its use and the order is pinned (sched_barrier), so several reads
+// stay in flight; left to itself the scheduler keeps one or two, and a wave
+// whose SIMD partner is not issuing MFMAs then waits on LDS latency before
+// most of them. frag(n) reads fragment n; op(n, a) issues MFMA n.
+template <int NF, int DEPTH, typename Frag, typename Op>
+__device__ __forceinline__ void lds_mfma_ring(Frag&& frag, Op&& op) {
+  bf16x8 ring[DEPTH];
+#pragma unroll
+  for (int n = 0; n < DEPTH; ++n) ring[n] = frag(n);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < NF; ++n) {
+    const bf16x8 a = ring[n % DEPTH];
+    if (n + DEPTH < NF) ring[n % DEPTH] = frag(n + DEPTH);
+    op(n, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 

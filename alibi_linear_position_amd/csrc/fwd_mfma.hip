@@ -410,14 +410,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
 
     // ---- S^T = K Q^T ----
     f32x16 s[KB];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (32 * kb + l32) * KPITCH + (16 * ks + 8 * hi) * 2);
-        s[kb] = mfma32(a, qf[ks], ks == 0 ? cinit : s[kb]);
-      }
-    }
+    lds_mfma_ring<KS * KB, 4>(
+        [&](int n) {
+          return *reinterpret_cast<const bf16x8*>(sK + (32 * (n % KB) + l32) * KPITCH + (16 * (n / KB) + 8 * hi) * 2);
+        },
+        [&](int n, const bf16x8& a) {
+          const int ks = n / KB, kb = n % KB;
+          s[kb] = mfma32(a, qf[ks], ks == 0 ? cinit : s[kb]);
+        });
 
     // ---- bias, mask, online softmax ----
     // Plain ALiBi: s = q.k + (c2 / c1)(8 (r / 4) + r % 4) and the exponent is
@@ -521,14 +521,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     l_run += lsum;
 
     // ---- O^T += V^T P^T, with the next tile's LDS stores in the same region ----
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int ps = 0; ps < PS; ++ps) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sV + (32 * db + l32) * VPITCH + (16 * ps + 8 * hi) * 2);
-        o[db] = mfma32(a, __builtin_bit_cast(bf16x8, pf[ps]), o[db]);
-      }
-    }
+    lds_mfma_ring<DB * PS, 4>(
+        [&](int n) {
+          return *reinterpret_cast<const bf16x8*>(sV + (32 * (n / PS) + l32) * VPITCH + (16 * (n % PS) + 8 * hi) * 2);
+        },
+        [&](int n, const bf16x8& a) { o[n / PS] = mfma32(a, __builtin_bit_cast(bf16x8, pf[n % PS]), o[n / PS]); });
     // After the last tile the registers still hold tile 0, which nobody reads
     // again; storing it keeps this region free of branches.
     regs.template store<KPITCH, VPITCH>(sKn, sKn + KBYTES, tid);
