@@ -283,7 +283,7 @@ const char* alibi_status_string(int status) {
   switch (status) {
     case ALIBI_OK: return "ALIBI_OK: success";
     case ALIBI_EINVAL: return "ALIBI_EINVAL: invalid argument (size, null or misaligned pointer)";
-    case ALIBI_ENOTSUP: return "ALIBI_ENOTSUP: request not supported by this build";
+    case ALIBI_ENOTSUP: return "ALIBI_ENOTSUP: request not supported by this library";
     case ALIBI_EHIP: return "ALIBI_EHIP: HIP runtime or launch failure";
     case ALIBI_ENOMEM: return "ALIBI_ENOMEM: decode workspace allocation failed";
     default: return "ALIBI: unknown status";

@@ -46,7 +46,7 @@ extern "C" {
 typedef enum alibi_status {
   ALIBI_OK = 0,
   ALIBI_EINVAL = -1,   /* bad size, null or misaligned pointer */
-  ALIBI_ENOTSUP = -2,  /* valid request this build does not handle (e.g. d > 256) */
+  ALIBI_ENOTSUP = -2,  /* valid request the library does not handle (e.g. d > 256) */
   ALIBI_EHIP = -3,     /* a HIP runtime call or kernel launch failed */
   ALIBI_ENOMEM = -4    /* the library could not allocate its decode workspace */
 } alibi_status;

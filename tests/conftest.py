@@ -18,7 +18,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) on a machine without a GPU when they are
-    # selected anyway; on a GPU machine they run.
+    # selected anyway; on a machine with a GPU they run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
