@@ -79,7 +79,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ALIBI_OK : ALIBI_EHIP; }
 
 // ---- library workspaces: growable buffers per device ----
 // kDecode holds the decode's partial softmax states, kNorm the key-norm maxima
-// of the skipping forward, kBwd the backward's row terms. Both are used asynchronously on the caller's stream.
+// of the skipping forward, kBwd the backward's row terms. All are used asynchronously on the caller's stream.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -285,7 +285,7 @@ const char* alibi_status_string(int status) {
     case ALIBI_EINVAL: return "ALIBI_EINVAL: invalid argument (size, null or misaligned pointer)";
     case ALIBI_ENOTSUP: return "ALIBI_ENOTSUP: request not supported by this library";
     case ALIBI_EHIP: return "ALIBI_EHIP: HIP runtime or launch failure";
-    case ALIBI_ENOMEM: return "ALIBI_ENOMEM: decode workspace allocation failed";
+    case ALIBI_ENOMEM: return "ALIBI_ENOMEM: workspace allocation failed";
     default: return "ALIBI: unknown status";
   }
 }

@@ -48,7 +48,7 @@ typedef enum alibi_status {
   ALIBI_EINVAL = -1,   /* bad size, null or misaligned pointer */
   ALIBI_ENOTSUP = -2,  /* valid request the library does not handle (e.g. d > 256) */
   ALIBI_EHIP = -3,     /* a HIP runtime call or kernel launch failed */
-  ALIBI_ENOMEM = -4    /* the library could not allocate its decode workspace */
+  ALIBI_ENOMEM = -4    /* the library could not allocate one of its workspaces */
 } alibi_status;
 
 /*
@@ -270,8 +270,9 @@ int alibi_debug_stream_read(const void* buf, long long bytes, unsigned* sink, in
 const char* alibi_status_string(int status);
 
 /*
- * Frees the library-owned decode workspaces on every device after a device
- * synchronisation. Safe to call at any time; later decode calls re-allocate.
+ * Frees the library-owned workspaces (decode partial states, key-norm maxima
+ * of the skipping forward, the backward's row terms) on every device after a
+ * device synchronisation. Safe to call at any time; later calls re-allocate.
  */
 int alibi_release(void);
 
