@@ -136,7 +136,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd16k", "decode", "copy", "bwd", "oracle"], default=None)
+    ap.add_argument("--only", choices=["fwd", "fwd16k", "c1", "c2", "c3", "decode", "copy", "bwd", "oracle"],
+                    default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -395,12 +396,20 @@ def run_only(args, alibi, W, fw, dw, dev):
     import torch
     if args.only == "oracle":
         return oracle_timing(W, dw, dev)
-    if args.only in ("fwd", "fwd16k"):
-        wl = fw if args.only == "fwd" else W.FWD_B1_H16_N16384_D128
+    if args.only in ("fwd", "fwd16k", "c2", "c3"):
+        wl = {"fwd": fw, "fwd16k": W.FWD_B1_H16_N16384_D128, "c2": W.FWD_B8_H8_N1024_D64,
+              "c3": W.FWD_B4_H12_N2048_D64}[args.only]
         q, k, v = (x.to(dev) for x in W.gaussian_qkv_bf16(wl.shape, seed=wl.seed))
         out = torch.empty_like(q)
         s = alibi.slopes(wl.H).to(dev)
         fn = lambda: alibi.attn_fwd(q, k, v, s, causal=True, out=out)
+        work, unit = fwd_flops(wl.B, wl.H, wl.N, wl.d), "flop"
+    elif args.only == "c1":
+        wl = W.TINY_FP32
+        q, k, v = (torch.from_numpy(x).reshape(wl.shape).to(dev) for x in W.tiny_example_qkv())
+        out = torch.empty_like(q)
+        s = alibi.slopes(wl.H).to(dev)
+        fn = lambda: alibi.attn_fwd_f32(q, k, v, s, causal=True, out=out)
         work, unit = fwd_flops(wl.B, wl.H, wl.N, wl.d), "flop"
     elif args.only == "decode":
         kc = W.device_gaussian_bf16((dw.B, dw.H, dw.L, dw.d), seed=dw.seed)
