@@ -46,6 +46,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // most of them. frag(n) reads fragment n; op(n, a) issues MFMA n.
 template <int NF, int DEPTH, typename Frag, typename Op>
 __device__ __forceinline__ void lds_mfma_ring(Frag&& frag, Op&& op) {
+  static_assert(NF >= DEPTH, "the prologue reads DEPTH fragments");
   bf16x8 ring[DEPTH];
 #pragma unroll
   for (int n = 0; n < DEPTH; ++n) ring[n] = frag(n);
