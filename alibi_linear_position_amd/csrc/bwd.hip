@@ -24,7 +24,8 @@
 // * bwd_dq_kernel: one workgroup per 128 queries, the forward's layout:
 //   S^T = K Q^T and dP^T = V dO^T (lane = query, so lse and D are one value
 //   per lane), dS^T packed to bf16 and dQ^T += K^T dS^T, with K^T read
-//   transposed from the row-major K tile; K and V staged per 64-key tile.
+//   transposed from the row-major K tile; K and V staged per 32-key tile
+//   (64-key tiles need more registers than two waves per SIMD leave).
 // Scores are in log2 units (c1 = log2(e) / sqrt(d), c2 = m log2(e)); masked and
 // out-of-range entries get P = 0.
 #include "device_common.h"
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dq, int H, int N, int nqb, int total, const float* __restrict__ slopes,
     float c1, float scale) {
-  constexpr int NT = 256, BM = 128, BN = 64;
+  constexpr int NT = 256, BM = 128, BN = 32;
   constexpr int KS = D / 16, KB = BN / 32, DB = D / 32, PS = BN / 16, CPR = D / 8;
   using Tile = SwzTile<D>;              // K and V tiles: swizzled rows of 2 D bytes
   constexpr int KBYTES = BN * Tile::ROWB;
@@ -482,13 +483,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         f32x16 s = cinit, dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + 32 * kb * Tile::ROWB + (rb ^ (32 * ks)));
-          s = mfma32(a, qf[ks], s);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(sV + 32 * kb * Tile::ROWB + (rb ^ (32 * ks)));
-          dp = mfma32(b, of[ks], dp);
-        }
+        // fragment 2 ks: K (for S), 2 ks + 1: V (for dP)
+        lds_mfma_ring<2 * KS, 2>(
+            [&](int n) {
+              return *reinterpret_cast<const bf16x8*>(((n & 1) ? sV : sK) + 32 * kb * Tile::ROWB + (rb ^ (32 * (n >> 1))));
+            },
+            [&](int n, const bf16x8& a) {
+              if (n & 1) dp = mfma32(a, of[n >> 1], dp);
+              else s = mfma32(a, qf[n >> 1], s);
+            });
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           float x[8];
@@ -510,12 +513,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
       }
       // ---- dQ^T += K^T dS^T ----
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps)
-          acc[db] = mfma32(read_tr<D>(sK, tb0, tb1, 16 * ps, 32 * db), __builtin_bit_cast(bf16x8, pf[ps]), acc[db]);
-      }
+      lds_mfma_ring<DB * PS, 2>(
+          [&](int n) { return read_tr<D>(sK, tb0, tb1, 16 * (n % PS), 32 * (n / PS)); },
+          [&](int n, const bf16x8& a) { acc[n / PS] = mfma32(a, __builtin_bit_cast(bf16x8, pf[n % PS]), acc[n / PS]); });
     }
     if (tile > 0) store_tile(smem + (stage ^ 1) * STAGE);
     stage ^= 1;
