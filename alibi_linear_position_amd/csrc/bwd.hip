@@ -428,6 +428,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  f32x16 dinit;  // dP^T seeded with -D, so the MFMA yields dP - D
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dinit[r] = -Dr;
 
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
@@ -482,7 +485,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       u32x4 pf[PS];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        f32x16 s = cinit, dp = f32x16{};
+        f32x16 s = cinit, dp = dinit;
         // fragment 2 ks: K (for S), 2 ks + 1: V (for dP)
         lds_mfma_ring<2 * KS, 2>(
             [&](int n) {
@@ -504,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
               if (!CAUSAL && jj > i) t -= 2.0f * c2 * float(jj - i);
               if (jj >= N || (CAUSAL && jj > i)) t = -__builtin_huge_valf();
             }
-            x[e] = fast_exp2(t) * (dp[r] - Dr);
+            x[e] = fast_exp2(t) * dp[r];
           }
           u32x4 pk;
 #pragma unroll
