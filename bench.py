@@ -29,6 +29,8 @@ same decode), scaled to the same units.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --only fwd|decode|copy|bwd [--steps K] [--warmup W]
+    python bench.py --only underflow     (CPU only: the bf16 underflow diagnostic
+                                          of the 16384-token workload, fp64 oracle)
 
 `--only` runs a single kernel (`bwd`: the three backward kernels; `copy`: a
 plain device-to-device copy of
@@ -136,17 +138,19 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd16k", "c1", "c2", "c3", "decode", "copy", "bwd", "oracle"],
-                    default=None)
+    ap.add_argument("--only", choices=["fwd", "fwd16k", "c1", "c2", "c3", "decode", "copy", "bwd", "oracle",
+                                       "underflow"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
+    import workloads as W
+    if args.only == "underflow":  # the oracle's diagnostic: CPU only, no library
+        return underflow_report(W)
     import torch
     import alibi_linear_position_amd as alibi
-    import workloads as W
 
     alibi.load_library()
     dev = torch.device("cuda:0")
@@ -389,6 +393,50 @@ def oracle_timing(W, dw, dev):
     record(dw.name, total, decode_bytes(dw.B, dw.H, dw.L, dw.d), "GB/s", threads,
            "1 run, host copies excluded")
     print(json.dumps(res), flush=True)
+
+
+def underflow_report(W):
+    """The bf16 underflow diagnostic of the 16384-token, 16-head workload (CPU only).
+
+    Per head, for the two thresholds tau_u = ln(smallest bf16 subnormal) and
+    tau_d = ln(smallest normal) ("When Attention Goes Blind", Sec. 3.2 and App. A
+    Table 4): the share of weights whose stable-softmax exponent lies at or below
+    the threshold, analytic (content scores 0: bias alone, -m d <= tau) and on the
+    seeded bf16 inputs (x_ij = s_ij - max_j s_ij <= tau), over the causal triangle
+    (Sec. 5.2's convention) and over the last row (Fig. 1b's per-distance
+    convention). The two steepest heads are flagged. Computed by the fp64 oracle.
+    """
+    import numpy as np
+    import oracle
+    wl = W.FWD_B1_H16_N16384_D128
+    q, k, _ = W.gaussian_qkv_bf16(wl.shape, seed=wl.seed)
+    slopes = oracle.slopes_ref(wl.H).astype(np.float64)
+    th = oracle.format_thresholds("bf16")
+    taus = {"tau_u": th["tau_u"], "tau_d": th["tau_d"]}
+    steep = set(int(x) for x in np.argsort(-slopes)[:2])
+    heads = []
+    t_all = time.perf_counter()
+    for h in range(wl.H):
+        m = float(slopes[h])
+        t0 = time.perf_counter()
+        data = oracle.underflow_fraction_data(q[0, h], k[0, h], m, [taus["tau_u"], taus["tau_d"]])
+        row = {"head": h, "slope": m, "steepest_two": h in steep}
+        for (name, tau), dd in zip(taus.items(), data):
+            row[name] = {
+                "analytic_triangle": oracle.underflow_fraction_causal(m, wl.N, tau),
+                "analytic_last_row": oracle.underflow_fraction_by_distance([m], wl.N, tau),
+                "data_triangle": dd["share"],
+                "data_last_row": dd["last_row_share"],
+            }
+        heads.append(row)
+        print(f"[underflow] head {h:2d} m={m:.6g}{' (steep)' if h in steep else ''}: "
+              f"tau_u tri {row['tau_u']['data_triangle']:.5f}/{row['tau_u']['analytic_triangle']:.5f} "
+              f"last {row['tau_u']['data_last_row']:.5f}/{row['tau_u']['analytic_last_row']:.5f}; "
+              f"tau_d tri {row['tau_d']['data_triangle']:.5f}/{row['tau_d']['analytic_triangle']:.5f} "
+              f"last {row['tau_d']['data_last_row']:.5f}/{row['tau_d']['analytic_last_row']:.5f} "
+              f"(data/analytic, {time.perf_counter() - t0:.1f} s)", flush=True)
+    print(json.dumps({"only": "underflow", "workload": wl.name, "thresholds": taus, "heads": heads,
+                      "seconds": round(time.perf_counter() - t_all, 1)}), flush=True)
 
 
 def run_only(args, alibi, W, fw, dw, dev):

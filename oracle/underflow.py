@@ -81,29 +81,33 @@ def underflow_fraction_causal(m: float, n: int, tau: float) -> float:
     return float(np.sum(count * hit) / np.sum(count))
 
 
-def underflow_fraction_data(q, k, m: float, tau: float, rows=None, causal=True) -> dict:
+def underflow_fraction_data(q, k, m: float, tau, rows=None, causal=True):
     """Data-dependent share of causal entries whose stable-softmax exponent is <= tau.
 
     For row i the exponent is x_ij = s_ij - max_j s_ij with s_ij the biased
     scaled score (Table 4's condition x <= tau_u). Returns the share over the
     chosen rows' causal entries and over the last chosen row alone. q, k: one
-    head, (N, d), any float type (upcast to fp64).
+    head, (N, d), any float type (upcast to fp64). ``tau`` may be a sequence
+    of thresholds: then one such dict per threshold, in order, from one pass.
     """
+    taus = [float(tau)] if np.isscalar(tau) else [float(t) for t in tau]
     import torch
     qf = q.detach().to("cpu", torch.float64).numpy() if isinstance(q, torch.Tensor) else np.asarray(q, np.float64)
     kf = k.detach().to("cpu", torch.float64).numpy() if isinstance(k, torch.Tensor) else np.asarray(k, np.float64)
     n, dk = qf.shape
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
-    hit = 0
+    hit = [0] * len(taus)
     tot = 0
-    last_share = 0.0
+    last_share = [0.0] * len(taus)
     for i in rows:
         nk = int(i) + 1 if causal else kf.shape[0]
         s = (kf[:nk] @ qf[i]) / math.sqrt(dk)
         s = s - float(m) * np.abs(int(i) - np.arange(nk, dtype=np.float64))
         x = s - np.max(s)
-        h = int(np.sum(x <= tau))
-        hit += h
+        for t, tv in enumerate(taus):
+            h = int(np.sum(x <= tv))
+            hit[t] += h
+            last_share[t] = h / nk
         tot += nk
-        last_share = h / nk
-    return {"share": hit / tot, "last_row_share": last_share}
+    res = [{"share": hit[t] / tot, "last_row_share": last_share[t]} for t in range(len(taus))]
+    return res[0] if np.isscalar(tau) else res

@@ -39,3 +39,22 @@ def test_flop_and_byte_conventions():
     assert bench.fwd_flops(8, 16, 4096, 128) == 4.0 * 128 * 8 * 16 * 4096 * 4097 / 2
     # K + V caches plus q and out
     assert bench.decode_bytes(1, 1, 10, 8) == 2 * 10 * 8 * 2 + 2 * 8 * 2
+
+
+def test_underflow_report_runs_on_a_small_workload(monkeypatch, capsys):
+    # the report's plumbing on a 2-head, 64-token stand-in of the workload
+    import json
+    sys.path.insert(0, ROOT)
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import bench
+    import workloads as W
+    small = W.FwdWorkload("small", 1, 2, 64, 16, "bf16")
+    monkeypatch.setattr(W, "FWD_B1_H16_N16384_D128", small)
+    bench.underflow_report(W)
+    rec = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert rec["only"] == "underflow" and len(rec["heads"]) == 2
+    h0 = rec["heads"][0]
+    assert h0["steepest_two"] and h0["slope"] == 2.0 ** -4
+    for name in ("tau_u", "tau_d"):
+        for key in ("analytic_triangle", "analytic_last_row", "data_triangle", "data_last_row"):
+            assert 0.0 <= h0[name][key] <= 1.0
