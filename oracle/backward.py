@@ -41,15 +41,25 @@ def lse_head_ref(q, k, m, causal=True):
     return (mx + np.log(np.sum(np.exp(logits - mx), axis=-1, keepdims=True)))[:, 0]
 
 
-def attn_backward_head_ref(q, k, v, do, m, causal=True):
-    """(dq, dk, dv) of one head for the upstream gradient do, fp64."""
+def attn_backward_head_ref(q, k, v, do, m, causal=True, magnitudes=False):
+    """(dq, dk, dv) of one head for the upstream gradient do, fp64.
+
+    With ``magnitudes`` also the sums of absolute products behind each gradient
+    element, (|dS| |K| / sqrt(d), |dS|^T |Q| / sqrt(d), P^T |dO|): the scale of
+    its terms, against which cancellation among them is measured (each bounds
+    the absolute value of its gradient).
+    """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     p = softmax_rows_ref(_logits(q, k, m, causal))
     dv = p.T @ do
     dp = do @ v.T
     ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
     scale = 1.0 / math.sqrt(q.shape[-1])
-    return ds @ k * scale, ds.T @ q * scale, dv
+    grads = (ds @ k * scale, ds.T @ q * scale, dv)
+    if not magnitudes:
+        return grads
+    a = np.abs(ds)
+    return grads, (a @ np.abs(k) * scale, a.T @ np.abs(q) * scale, p.T @ np.abs(do))
 
 
 def attn_backward_ref(q, k, v, do, slopes, causal=True):

@@ -34,5 +34,30 @@ def check_bf16(gpu, ref, label):
     return float(err.max())
 
 
+class Bf16Stats:
+    """The bf16 bar of check_bf16 accumulated over the pieces of one large
+    configuration (one (b, h) at a time keeps host memory bounded)."""
+
+    def __init__(self, label):
+        self.label, self.max_err, self.over, self.failing, self.n = label, 0.0, 0, 0, 0
+
+    def add(self, gpu, ref):
+        g = gpu.detach().to("cpu", torch.float64).numpy() if isinstance(gpu, torch.Tensor) else np.asarray(gpu)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert g.shape == ref.shape, (g.shape, ref.shape)
+        assert np.all(np.isfinite(g)), f"{self.label}: non-finite output"
+        err = np.abs(g - ref)
+        self.max_err = max(self.max_err, float(err.max()))
+        self.over += int(np.sum(err > BF16_TOL))
+        self.failing += int(np.sum(err > BF16_TOL + half_ulp_bf16(ref)))
+        self.n += err.size
+
+    def finish(self):
+        print(f"[parity] {self.label}: {self.n} elements, max|err|={self.max_err:.3e} "
+              f"elements>1e-2={self.over} failing={self.failing}", flush=True)
+        assert self.failing == 0, f"{self.label}: {self.failing} elements beyond tolerance, max err {self.max_err}"
+        return self.max_err
+
+
 def dev(x):
     return x.to("cuda").contiguous()

@@ -3,8 +3,16 @@
 Gradients of the plain causal (and symmetric) ALiBi forward against the fp64
 oracle's chain rule (oracle/backward.py, pinned to autograd and finite
 differences). The pages state no tolerance for gradients; the bar used here is
-|gpu - o| <= 1e-2 + 1e-2 |o| per element: the bf16 output rounding alone is
-2^-9 |o|, and P and dS enter the MFMAs as bf16. The log-sum-exp comes from the
+derived from the arithmetic, per element:
+    |gpu - o| <= 1e-2 + 1e-2 (|o| + M),
+with M the sum of absolute products behind the element (|dS| |K| / sqrt(d) for
+dq, |dS|^T |Q| / sqrt(d) for dk, P^T |dO| for dv; oracle magnitudes). The bf16
+rounding of the output is 2^-9 |o|; but dS and P enter the MFMAs rounded to
+bf16 (2^-9 relative) and P is recomputed from the forward's log-sum-exp
+(relative error up to the 2.5e-3 bar below), errors that scale with the terms,
+M, not with their sum |o|: where the terms cancel (a steep head's dq at
+N = 4096) they dominate. The absolute 1e-2 covers D = rowsum(dO O) taken from
+the forward's bf16 output. The log-sum-exp comes from the
 forward's running maximum and its row sum of bf16-rounded weights, whose
 relative error is at most 2^-9 (a sum of positive terms), so |err| <= ln(1 +
 2^-9) = 1.95e-3 plus fp32 rounding: the bar is 2.5e-3.
@@ -31,13 +39,23 @@ def alibi():
     return mod
 
 
-def check_grad(gpu, ref, label):
+def check_grad(gpu, ref, label, mag=None):
+    """mag: the oracle's magnitude sums for these elements (None: |ref| bounds them)."""
     g = gpu.detach().to("cpu", torch.float64).numpy()
     err = np.abs(g - ref)
-    bad = int(np.sum(err > G_ATOL + G_RTOL * np.abs(ref)))
-    print(f"[parity] {label}: max|err|={err.max():.3e} max|ref|={np.abs(ref).max():.3e} failing={bad}",
-          flush=True)
+    m = np.abs(ref) if mag is None else np.asarray(mag)
+    bar = G_ATOL + G_RTOL * (np.abs(ref) + m)
+    bad = int(np.sum(err > bar))
+    over_old = int(np.sum(err > G_ATOL + G_RTOL * np.abs(ref)))
+    print(f"[parity] {label}: max|err|={err.max():.3e} max|ref|={np.abs(ref).max():.3e} "
+          f"max err/bar={np.max(err / bar):.3f} beyond 1e-2+1e-2|o|: {over_old} failing={bad}", flush=True)
     assert np.all(np.isfinite(g)) and bad == 0, label
+
+
+def check_grads(gpu3, q, k, v, do, m, causal, label):
+    (rq, rk, rv), (mq, mk, mv) = oracle.attn_backward_head_ref(q, k, v, do, m, causal, magnitudes=True)
+    for g, r, mg, n in zip(gpu3, (rq, rk, rv), (mq, mk, mv), ("dq", "dk", "dv")):
+        check_grad(g, r, f"{n} {label}", mg)
 
 
 def _inputs(shape, seed):
@@ -60,17 +78,19 @@ def test_backward_small(alibi, B, H, N, d, causal):
     out, lse = alibi.attn_fwd_train(qd, kd, vd, torch.from_numpy(s), causal)
     dq, dk, dv = alibi.attn_bwd(qd, kd, vd, out, dod, lse, torch.from_numpy(s), causal)
     torch.cuda.synchronize()
-    rq, rk, rv = oracle.attn_backward_ref(q, k, v, do, s, causal)
     tag = f"B{B} H{H} N{N} d{d} causal={causal}"
-    check_grad(dq, rq, "dq " + tag)
-    check_grad(dk, rk, "dk " + tag)
-    check_grad(dv, rv, "dv " + tag)
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for b in range(B):
+        for h in range(H):
+            check_grads((dq[b, h], dk[b, h], dv[b, h]), q[b, h], k[b, h], v[b, h], do[b, h], float(s[h]), causal,
+                        f"{tag} b={b} h={h}")
     lerr = np.abs(lse.cpu().double().numpy() - oracle.lse_ref(q, k, s, causal)).max()
     print(f"[parity] lse {tag}: max err {lerr:.2e}", flush=True)
     assert lerr <= LSE_TOL
 
 
-def test_backward_full_size_two_heads(alibi):
+def test_backward_benchmark_shape_every_head(alibi):
+    # the sequence shape of the benchmark (N = 4096, d = 128), all 16 heads of one batch
     wl = W.FWD_B8_H16_N4096_D128
     shape = (1, wl.H, wl.N, wl.d)
     q, k, v, do = _inputs(shape, wl.seed)
@@ -78,12 +98,10 @@ def test_backward_full_size_two_heads(alibi):
     qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
     out, lse = alibi.attn_fwd_train(qd, kd, vd, torch.from_numpy(s), True)
     dq, dk, dv = alibi.attn_bwd(qd, kd, vd, out, dod, lse, torch.from_numpy(s), True)
-    torch.cuda.synchronize()
-    for h in (0, wl.H - 1):
-        rq, rk, rv = oracle.attn_backward_head_ref(q[0, h], k[0, h], v[0, h], do[0, h], float(s[h]), True)
-        check_grad(dq[0, h], rq, f"dq N4096 h={h}")
-        check_grad(dk[0, h], rk, f"dk N4096 h={h}")
-        check_grad(dv[0, h], rv, f"dv N4096 h={h}")
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for h in range(wl.H):
+        check_grads((dq[0, h], dk[0, h], dv[0, h]), q[0, h], k[0, h], v[0, h], do[0, h], float(s[h]), True,
+                    f"N4096 h={h}")
 
 
 def test_forward_with_lse_is_the_same_forward(alibi):

@@ -96,3 +96,20 @@ def test_lse_against_scipy_and_weights():
     assert np.allclose(lse, logsumexp(logits, axis=1), atol=1e-12)
     _, w = oracle.attn_head_ref(q, k, v, m, True)
     assert np.allclose(np.where(j <= i, np.exp(logits - lse[:, None]), 0.0), w, atol=1e-13)
+
+
+def test_backward_magnitudes_bound_the_gradients():
+    # |sum_j a_j b_j| <= sum_j |a_j| |b_j|: each magnitude bounds its gradient,
+    # with equality where no terms cancel (all of one sign: dv with do >= 0)
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((24, 8)) for _ in range(3))
+    do = rng.standard_normal((24, 8))
+    for causal in (True, False):
+        (dq, dk, dv), (mq, mk, mv) = oracle.attn_backward_head_ref(q, k, v, do, 0.3, causal, magnitudes=True)
+        assert np.all(np.abs(dq) <= mq * (1 + 1e-12)) and np.all(np.abs(dk) <= mk * (1 + 1e-12))
+        assert np.all(np.abs(dv) <= mv * (1 + 1e-12))
+        plain = oracle.attn_backward_head_ref(q, k, v, do, 0.3, causal)
+        for a, b in zip(plain, (dq, dk, dv)):
+            assert np.array_equal(a, b)
+    (_, _, dv), (_, _, mv) = oracle.attn_backward_head_ref(q, k, v, np.abs(do), 0.3, True, magnitudes=True)
+    assert np.allclose(dv, mv, rtol=1e-13)
