@@ -15,6 +15,8 @@ or a call returns an error status, these functions raise.
     attn_fwd_train(q, k, v, slopes, causal) -> (out, lse)
     attn_bwd(q, k, v, out, dout, lse, slopes, causal) -> (dq, dk, dv)
     attn_decode(q, kcache, vcache, slopes)  -> bf16 (B, H, d)
+    decode_ws_bytes(B, H, L, d), attn_decode_ws(q, kcache, vcache, ws, slopes)
+                                           -> the decode with a caller-owned workspace
     attn_weights_f32(q, k, slopes, causal)  -> fp32 (B, H, N, N), test only
 """
 from __future__ import annotations
@@ -23,7 +25,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libalibi.so")
+# ALIBI_LIBRARY names another build of the same library (e.g. an instrumented
+# test build); by default the in-tree libalibi.so.
+LIB_PATH = os.environ.get("ALIBI_LIBRARY") or os.path.join(HERE, "libalibi.so")
 
 ALIBI_OK = 0
 _STATUS = {0: "ALIBI_OK", -1: "ALIBI_EINVAL", -2: "ALIBI_ENOTSUP", -3: "ALIBI_EHIP", -4: "ALIBI_ENOMEM"}
@@ -46,7 +50,11 @@ EXPORTS = {
     "alibi_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
     "alibi_status_string": [_I],
     "alibi_release": [],
+    "alibi_decode_ws_bytes": [_I, _I, _I, _I],
+    "alibi_attn_decode_ws": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_size_t, _P],
+    "alibi_debug_fail_allocations": [_I],
 }
+_RESTYPES = {"alibi_status_string": ctypes.c_char_p, "alibi_decode_ws_bytes": ctypes.c_size_t}
 
 # mitigation bits of alibi_fwd_opts.flags and the slope recipes (include/alibi.h)
 CLAMP, LOG_DISTANCE, SOFTCAP, SKIP_UNDERFLOW = 1, 2, 4, 8
@@ -79,7 +87,7 @@ def load_library(path: str = LIB_PATH):
     for name, argtypes in EXPORTS.items():
         fn = getattr(lib, name)
         fn.argtypes = argtypes
-        fn.restype = ctypes.c_char_p if name == "alibi_status_string" else ctypes.c_int
+        fn.restype = _RESTYPES.get(name, ctypes.c_int)
     _lib = lib
     return lib
 
@@ -271,6 +279,37 @@ def attn_decode(q, kcache, vcache, slopes=None, out=None):
             _P(q.data_ptr()), _P(kcache.data_ptr()), _P(vcache.data_ptr()), _P(out.data_ptr()),
             B, H, L, d, _P(s.data_ptr()), _stream_handle(q.device))
     _check("alibi_attn_decode", st)
+    return out
+
+
+def decode_ws_bytes(B, H, L, d):
+    """Bytes of device workspace attn_decode_ws needs for this shape (0: none)."""
+    return int(load_library().alibi_decode_ws_bytes(int(B), int(H), int(L), int(d)))
+
+
+def attn_decode_ws(q, kcache, vcache, ws, slopes=None, out=None):
+    """attn_decode with a caller-owned workspace: ws, a device tensor of at least
+    decode_ws_bytes(...) bytes (or None when that is 0)."""
+    import torch
+    _need(q, torch.bfloat16, 3, "q")
+    _need(kcache, torch.bfloat16, 4, "kcache")
+    _need(vcache, torch.bfloat16, 4, "vcache")
+    B, H, L, d = kcache.shape
+    if vcache.shape != kcache.shape or tuple(q.shape) != (B, H, d):
+        raise ValueError("expected q (B, H, d) and caches (B, H, L, d)")
+    s = _slopes_dev(slopes, H, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, torch.bfloat16, 3, "out")
+    if ws is not None and (not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous device tensor")
+    ptr, nbytes = (0, 0) if ws is None else (ws.data_ptr(), ws.numel() * ws.element_size())
+    with torch.cuda.device(q.device):
+        st = load_library().alibi_attn_decode_ws(
+            _P(q.data_ptr()), _P(kcache.data_ptr()), _P(vcache.data_ptr()), _P(out.data_ptr()),
+            B, H, L, d, _P(s.data_ptr()), _P(ptr), ctypes.c_size_t(nbytes), _stream_handle(q.device))
+    _check("alibi_attn_decode_ws", st)
     return out
 
 

@@ -41,25 +41,35 @@ def compile_flags():
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libalibi.so; returns its path."""
+def build(verbose: bool = False, out: str = LIB, extra_flags=(), jobs: int = 0) -> str:
+    """Compile every source and link the shared library (libalibi.so next to
+    this file by default); returns its path. extra_flags are added to every
+    compile and to the link (e.g. host-only instrumentation of a test build);
+    jobs: parallel compiles (0 = one per available core, at most 8)."""
+    from concurrent.futures import ThreadPoolExecutor
     cc = hipcc()
+    extra = list(extra_flags)
+    if jobs <= 0:
+        jobs = max(1, min(8, len(os.sched_getaffinity(0))))
     with tempfile.TemporaryDirectory(prefix="alibi_build_") as tmp:
+        cmds = []
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            cmd = [cc, *compile_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+            cmds.append([cc, *compile_flags(), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+            objs.append(obj)
+
+        def run(cmd):
             if verbose:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True)
-            objs.append(obj)
-        tmp_lib = LIB + ".tmp"
-        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
-        os.replace(tmp_lib, LIB)
-    return LIB
+
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            list(pool.map(run, cmds))
+        tmp_lib = out + ".tmp"
+        run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *extra, *objs, "-o", tmp_lib])
+        os.replace(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -87,8 +88,12 @@ struct Workspace {
 enum { kDecode = 0, kNorm = 1, kBwd = 2, kNumWorkspaces = 3 };
 std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws[kNumWorkspaces];
+// Test hook (alibi_debug_fail_allocations): workspace requests left to fail.
+std::atomic<int> g_fail_allocs{0};
 
 int workspace_get(int which, size_t bytes, float** out) {
+  for (int n = g_fail_allocs.load(); n > 0;)
+    if (g_fail_allocs.compare_exchange_weak(n, n - 1)) return ALIBI_ENOMEM;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ALIBI_EHIP;
   std::vector<Workspace>& list = g_ws[which];
@@ -111,6 +116,33 @@ int workspace_get(int which, size_t bytes, float** out) {
   }
   *out = static_cast<float*>(w.ptr);
   return ALIBI_OK;
+}
+
+// Validation shared by the decode entry points.
+int check_decode(const void* q, const void* kcache, const void* vcache, const void* out, const float* slopes,
+                 int B, int H, int L, int d) {
+  const int st = check_common(q, kcache, vcache, out, slopes, B, H, L, d, 16);
+  if (st != ALIBI_OK) return st;
+  if (d > 256 || d % 8 != 0) return ALIBI_ENOTSUP;
+  return ALIBI_OK;
+}
+
+// Bytes of partial softmax states the decode needs for this shape: 0 when a
+// (b, h) is not split across workgroups.
+size_t decode_ws_bytes(int B, int H, int L, int d) {
+  int splits = 1, chunk = L;
+  alibi::decode_plan(B, H, L, d, &splits, &chunk);
+  return splits > 1 ? (size_t)B * H * splits * (d + 2) * sizeof(float) : 0;
+}
+
+int launch_decode_plan(const void* q, const void* kcache, const void* vcache, void* out, int B, int H, int L,
+                       int d, const float* slopes, float* ws, hipStream_t stream) {
+  int splits = 1, chunk = L;
+  alibi::decode_plan(B, H, L, d, &splits, &chunk);
+  if (log_enabled())
+    std::fprintf(stderr, "[alibi] decode B=%d H=%d L=%d d=%d splits=%d chunk=%d\n", B, H, L, d, splits, chunk);
+  return hip_status(alibi::launch_decode(q, kcache, vcache, out, ws, B, H, L, d, splits, chunk, slopes,
+                                         scale_log2(d), stream));
 }
 
 }  // namespace
@@ -228,22 +260,31 @@ int alibi_slopes_recipe(int recipe, int H, int log_distance, float* slopes_out) 
 
 int alibi_attn_decode(const void* q, const void* kcache, const void* vcache, void* out, int B,
                       int H, int L, int d, const float* slopes, hipStream_t stream) {
-  int st = check_common(q, kcache, vcache, out, slopes, B, H, L, d, 16);
+  int st = check_decode(q, kcache, vcache, out, slopes, B, H, L, d);
   if (st != ALIBI_OK) return st;
-  if (d > 256 || d % 8 != 0) return ALIBI_ENOTSUP;
-  int splits = 1, chunk = L;
-  alibi::decode_plan(B, H, L, d, &splits, &chunk);
   float* ws = nullptr;
-  if (splits > 1) {
+  const size_t bytes = decode_ws_bytes(B, H, L, d);
+  if (bytes > 0) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    const size_t bytes = (size_t)B * H * splits * (d + 2) * sizeof(float);
     st = workspace_get(kDecode, bytes, &ws);
     if (st != ALIBI_OK) return st;
   }
-  if (log_enabled())
-    std::fprintf(stderr, "[alibi] decode B=%d H=%d L=%d d=%d splits=%d chunk=%d\n", B, H, L, d, splits, chunk);
-  return hip_status(alibi::launch_decode(q, kcache, vcache, out, ws, B, H, L, d, splits, chunk, slopes,
-                                         scale_log2(d), stream));
+  return launch_decode_plan(q, kcache, vcache, out, B, H, L, d, slopes, ws, stream);
+}
+
+size_t alibi_decode_ws_bytes(int B, int H, int L, int d) {
+  if (B < 1 || H < 1 || L < 1 || d < 1 || L > kMaxLen || d > 256 || d % 8 != 0) return 0;
+  return decode_ws_bytes(B, H, L, d);
+}
+
+int alibi_attn_decode_ws(const void* q, const void* kcache, const void* vcache, void* out, int B, int H,
+                         int L, int d, const float* slopes, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_decode(q, kcache, vcache, out, slopes, B, H, L, d);
+  if (st != ALIBI_OK) return st;
+  const size_t bytes = decode_ws_bytes(B, H, L, d);
+  if (bytes > 0 && (ws == nullptr || !aligned(ws, 16) || ws_bytes < bytes)) return ALIBI_EINVAL;
+  return launch_decode_plan(q, kcache, vcache, out, B, H, L, d, slopes, bytes > 0 ? static_cast<float*>(ws) : nullptr,
+                            stream);
 }
 
 int alibi_attn_weights_f32(const float* q, const float* k, float* w, int B, int H, int N, int d,
@@ -271,6 +312,12 @@ int alibi_debug_stream_read(const void* buf, long long bytes, unsigned* sink, in
       (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
     return ALIBI_EINVAL;
   return hip_status(alibi::launch_stream_read(buf, bytes, sink, workgroups, stream));
+}
+
+int alibi_debug_fail_allocations(int count) {
+  if (count < 0) return ALIBI_EINVAL;
+  g_fail_allocs.store(count);
+  return ALIBI_OK;
 }
 
 int alibi_debug_fwd_waves(int nw) {

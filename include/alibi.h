@@ -103,11 +103,31 @@ int alibi_attn_fwd_f32(const float* q, const float* k, const float* v, float* ou
  * cannot be allocated. Calls on one device are serialised by a mutex while
  * they size the workspace; the work itself stays asynchronous, and every
  * decode on one device uses the same workspace: order such calls on one
- * stream (or synchronise between them).
+ * stream (or synchronise between them), or give each stream its own workspace
+ * through alibi_attn_decode_ws.
  */
 int alibi_attn_decode(const void* q, const void* kcache, const void* vcache, void* out,
                       int B, int H, int L, int d, const float* slopes,
                       hipStream_t stream);
+
+/*
+ * The same decode with a caller-owned workspace instead of the library's: no
+ * allocation, no lock, and concurrent decodes on different streams stay
+ * independent as long as each has its own workspace.
+ * alibi_decode_ws_bytes(B, H, L, d) gives the bytes the call needs for a shape
+ * (the partial softmax states of a key range split, B H S (d + 2) fp32 values
+ * for S ranges per (b, h); 0 when no (b, h) is split, and 0 for arguments the
+ * decode rejects). ws: device memory of at least that many bytes, 16-byte
+ * aligned, owned by the caller and used asynchronously on `stream` (keep it
+ * alive until the call's work completes); may be NULL when 0 bytes are needed.
+ * Errors: as alibi_attn_decode, plus ALIBI_EINVAL for a missing, misaligned or
+ * too small workspace. Source: the KV-cache remark of abhik.ai after the
+ * full-sequence example (serving-style decode, where concurrent streams occur).
+ */
+size_t alibi_decode_ws_bytes(int B, int H, int L, int d);
+int alibi_attn_decode_ws(const void* q, const void* kcache, const void* vcache, void* out,
+                         int B, int H, int L, int d, const float* slopes,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * TEST ONLY, not on the hot path: materialises the fp32 attention weights
@@ -239,6 +259,14 @@ int alibi_slopes_recipe(int recipe, int H, int log_distance, float* slopes_out);
  * outside [0, nbh nblk), sizes < 1 or NULL.
  */
 int alibi_debug_schedule(int w, int nbh, int nblk, int* out2);
+
+/*
+ * TEST ONLY: the next `count` requests for a library-owned workspace (decode,
+ * skipping forward, backward) fail with ALIBI_ENOMEM as if the device
+ * allocation had failed, before any HIP call; 0 turns the hook off.
+ * Process-wide. ALIBI_EINVAL for count < 0.
+ */
+int alibi_debug_fail_allocations(int count);
 
 /*
  * TEST AND TUNING ONLY: waves per workgroup of the bf16 MFMA forward kernel,

@@ -25,7 +25,7 @@ def lib():
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(alibi_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(alibi_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_boundary():
@@ -236,3 +236,81 @@ def test_stream_read_validation(lib):
     assert f(ok_buf, 64, P(8194), 4, None) == -1        # sink not 4-byte aligned
     assert f(ok_buf, 64, ok_sink, 0, None) == -1
     assert f(ok_buf, 64, ok_sink, 65537, None) == -1
+
+
+def _bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=1, N=8,
+         d=64, s=FAKE, causal=1):
+    return lib.alibi_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, s, causal, None)
+
+
+def test_bwd_validation(lib):
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "s"):
+        assert _bwd(lib, **{name: None}) == -1, name
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        assert _bwd(lib, **{name: FAKE + 8}) == -1, name   # 16-byte alignment of the bf16 tensors
+    assert _bwd(lib, lse=FAKE + 2) == -1                   # fp32 lse: 4-byte alignment
+    assert _bwd(lib, s=FAKE + 2) == -1
+    for bad in (dict(B=0), dict(H=-1), dict(N=0), dict(d=0), dict(N=(1 << 24) + 1), dict(causal=2)):
+        assert _bwd(lib, **bad) == -1, bad
+    assert _bwd(lib, d=96) == -2                           # the backward handles d = 64 and 128
+    assert _bwd(lib, d=256) == -2
+
+
+def test_decode_ws_sizes_and_validation(lib):
+    # c5 (B32 H32 L32768 d128): 4 key ranges per (b, h), (d + 2) fp32 states each
+    assert lib.alibi_decode_ws_bytes(32, 32, 32768, 128) == 32 * 32 * 4 * 130 * 4
+    assert lib.alibi_decode_ws_bytes(64, 64, 32768, 128) == 0   # 4096 (b, h): no split
+    assert lib.alibi_decode_ws_bytes(1, 1, 300, 128) == 2 * 130 * 4
+    for bad in ((0, 1, 8, 128), (1, 0, 8, 128), (1, 1, 0, 128), (1, 1, 8, 127), (1, 1, 8, 264),
+                (1, 1, (1 << 24) + 1, 128)):
+        assert lib.alibi_decode_ws_bytes(*bad) == 0, bad
+    f = lib.alibi_attn_decode_ws
+    need = lib.alibi_decode_ws_bytes(1, 1, 300, 128)
+    assert f(None, FAKE, FAKE, FAKE, 1, 1, 300, 128, FAKE, FAKE, need, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 300, 127, FAKE, FAKE, need, None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 300, 128, FAKE, None, need, None) == -1       # missing
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 300, 128, FAKE, FAKE + 4, need, None) == -1   # misaligned
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 300, 128, FAKE, FAKE, need - 4, None) == -1   # too small
+
+
+def test_debug_fail_allocations_validation(lib):
+    assert lib.alibi_debug_fail_allocations(-1) == -1
+    assert lib.alibi_debug_fail_allocations(0) == 0
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+def test_enomem_from_the_allocation_hook(lib):
+    # every library workspace request fails while the hook is armed; nothing is launched
+    split = dict(B=1, H=1, L=100000, d=128)   # a split decode needs the workspace
+    dec = lambda: lib.alibi_attn_decode(FAKE, FAKE, FAKE, FAKE, split["B"], split["H"], split["L"], split["d"],
+                                        FAKE, None)
+    import alibi_linear_position_amd as alibi
+    opts = alibi.FwdOpts()
+    opts.flags = alibi.SKIP_UNDERFLOW
+    skip = lambda: lib.alibi_attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, 1, 1, 512, 512, 128, FAKE, 1, ctypes.byref(opts), None)
+    try:
+        assert lib.alibi_debug_fail_allocations(3) == 0
+        assert dec() == -4
+        assert skip() == -4
+        assert _bwd(lib, d=128) == -4
+    finally:
+        assert lib.alibi_debug_fail_allocations(0) == 0
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the error path of a machine without a GPU")
+def test_ehip_without_a_gpu(lib):
+    # valid arguments reach the first HIP call, which fails on a machine with no device
+    assert _fwd(lib) == -3
+    assert _fwd(lib, "alibi_attn_fwd_f32", d=16) == -3
+    assert lib.alibi_attn_decode(FAKE, FAKE, FAKE, FAKE, 1, 1, 100000, 128, FAKE, None) == -3
+    need = lib.alibi_decode_ws_bytes(1, 1, 300, 128)
+    assert lib.alibi_attn_decode_ws(FAKE, FAKE, FAKE, FAKE, 1, 1, 300, 128, FAKE, FAKE, need, None) == -3
+    assert _bwd(lib, d=128) == -3
+    assert lib.alibi_release() == 0
