@@ -1,11 +1,13 @@
-// Plain streaming read of a device buffer: the practical HBM read ceiling the
-// decode's bandwidth is read against. Measurement tool only, not on the
+// Plain streaming read of a device buffer: the practical HBM read rate against
+// which the decode's bandwidth is read. Measurement tool only, not on the
 // attention path.
 //
-// Each thread reads 16-byte chunks, eight in flight, in a grid-stride loop
-// that visits every chunk exactly once. A workgroup writes the XOR of all words
-// it read to sink[workgroup], so the loads cannot be optimised away and the XOR
-// of the sink equals the XOR of the buffer.
+// It reads the way the decode does: each workgroup streams one contiguous slab
+// of the buffer (bytes / workgroups, 16-byte aligned), every thread keeps eight
+// non-temporal 16-byte loads in flight, and consecutive lanes read consecutive
+// chunks. Every chunk is read exactly once. A workgroup writes the XOR of all
+// words it read to sink[workgroup], so the loads cannot be optimised away and
+// the XOR of the sink equals the XOR of the buffer.
 #include "device_common.h"
 #include "launch.h"
 
@@ -17,18 +19,19 @@ constexpr int kReadThreads = 256;
 constexpr int kReadUnroll = 8;
 
 __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* __restrict__ p, long long n16,
-                                                                   uint32_t* __restrict__ sink) {
+                                                                   long long slab, uint32_t* __restrict__ sink) {
   constexpr int U = kReadUnroll;
   __shared__ uint32_t red[kReadThreads / 64];
   const int tid = threadIdx.x;
-  const long long stride = (long long)gridDim.x * kReadThreads * U;
+  const long long beg = (long long)blockIdx.x * slab;
+  const long long end = beg + slab < n16 ? beg + slab : n16;
   u32x4 a = {0u, 0u, 0u, 0u};
-  for (long long i = (long long)blockIdx.x * kReadThreads * U + tid; i < n16; i += stride) {
+  for (long long i = beg + tid; i < end; i += (long long)kReadThreads * U) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const long long j = i + (long long)u * kReadThreads;
-      v[u] = j < n16 ? p[j] : u32x4{0u, 0u, 0u, 0u};
+      v[u] = j < end ? __builtin_nontemporal_load(p + j) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) a ^= v[u];
@@ -49,8 +52,10 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
 }  // namespace
 
 hipError_t launch_stream_read(const void* buf, long long bytes, uint32_t* sink, int workgroups, hipStream_t stream) {
+  const long long n16 = bytes / 16;
+  const long long slab = (n16 + workgroups - 1) / workgroups;
   hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(workgroups)), dim3(kReadThreads), 0, stream,
-                     static_cast<const u32x4*>(buf), bytes / 16, sink);
+                     static_cast<const u32x4*>(buf), n16, slab, sink);
   return hipGetLastError();
 }
 

@@ -231,8 +231,10 @@ def main():
                                 "per_launch": f"{nbytes:.4e} B",
                                 "read_ceiling": {"value": round(read_gbs, 1), "unit": "GB/s",
                                                  "kernel": "stream_read_kernel",
-                                                 "note": "plain streaming read of the same K and V caches; "
-                                                         "context, not the peak"}}},
+                                                 "note": "plain streaming read of the same K and V caches the "
+                                                         "way the decode reads them (a contiguous slab per "
+                                                         "workgroup, non-temporal 16-byte loads, 8 in flight "
+                                                         "per thread); context, not the peak"}}},
         "cpu_baseline": None,
     }
     res["next"] = next_forms(alibi, qg, kg, vg, s_f, fw)

@@ -181,3 +181,38 @@ def test_fwd_far_key_dominates_rows(alibi, fwd_waves):
     out = alibi.attn_fwd(dev(qb), dev(kb), dev(vb), torch.from_numpy(s), causal=True)
     ref = oracle.attn_ref(qb, kb, vb, s, causal=True)
     check_bf16(out, ref, "far key dominates")
+
+
+@pytest.mark.parametrize("B,H,L,d", [(2, 3, 300, 128), (1, 1, 70000, 128), (3, 5, 513, 32), (64, 64, 40, 64)])
+def test_decode_caller_workspace_matches_library_workspace(alibi, B, H, L, d):
+    # the same kernels on a workspace the caller owns: bitwise-equal output
+    q, kc, vc = W.gaussian_qkv_bf16((B, H, d), seed=B * 7 + L, kv_shape=(B, H, L, d))
+    s = alibi.slopes(H)
+    qd, kd, vd = dev(q), dev(kc), dev(vc)
+    need = alibi.decode_ws_bytes(B, H, L, d)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda") if need > 0 else None
+    a = alibi.attn_decode(qd, kd, vd, s)
+    b = alibi.attn_decode_ws(qd, kd, vd, ws, s)
+    torch.cuda.synchronize()
+    print(f"[parity] decode ws B{B} H{H} L{L} d{d}: {need} workspace bytes", flush=True)
+    assert torch.equal(a, b)
+    check_bf16(b, oracle.decode_ref(q, kc, vc, oracle.slopes_ref(H)), f"decode ws B{B} H{H} L{L} d{d}")
+
+
+def test_decode_caller_workspaces_on_two_streams(alibi):
+    # two decodes in flight at once on two streams, each with its own workspace
+    shapes = [(2, 4, 9000, 128, 61), (1, 8, 20000, 64, 62)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs, refs = [], []
+    for (B, H, L, d, seed), st in zip(shapes, streams):
+        q, kc, vc = W.gaussian_qkv_bf16((B, H, d), seed=seed, kv_shape=(B, H, L, d))
+        refs.append(oracle.decode_ref(q, kc, vc, oracle.slopes_ref(H)))
+        qd, kd, vd = dev(q), dev(kc), dev(vc)
+        ws = torch.empty(max(alibi.decode_ws_bytes(B, H, L, d), 16), dtype=torch.uint8, device="cuda")
+        sl = alibi.slopes(H).cuda()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            outs.append((alibi.attn_decode_ws(qd, kd, vd, ws, sl), ws, qd, kd, vd, sl))
+    torch.cuda.synchronize()
+    for (o, *_), ref, (B, H, L, d, _) in zip(outs, refs, shapes):
+        check_bf16(o, ref, f"decode ws two streams B{B} H{H} L{L} d{d}")
