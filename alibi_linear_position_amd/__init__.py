@@ -53,6 +53,7 @@ EXPORTS = {
     "alibi_decode_ws_bytes": [_I, _I, _I, _I],
     "alibi_attn_decode_ws": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_size_t, _P],
     "alibi_debug_fail_allocations": [_I],
+    "alibi_attn_decode_noalloc": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
 }
 _RESTYPES = {"alibi_status_string": ctypes.c_char_p, "alibi_decode_ws_bytes": ctypes.c_size_t}
 
@@ -279,6 +280,29 @@ def attn_decode(q, kcache, vcache, slopes=None, out=None):
             _P(q.data_ptr()), _P(kcache.data_ptr()), _P(vcache.data_ptr()), _P(out.data_ptr()),
             B, H, L, d, _P(s.data_ptr()), _stream_handle(q.device))
     _check("alibi_attn_decode", st)
+    return out
+
+
+def attn_decode_noalloc(q, kcache, vcache, slopes_dev, out):
+    """attn_decode through the entry point that allocates nothing: slopes_dev (H
+    fp32 on q's device) and out (bf16 (B, H, d)) are passed in, so this call
+    allocates no device memory either."""
+    import torch
+    _need(q, torch.bfloat16, 3, "q")
+    _need(kcache, torch.bfloat16, 4, "kcache")
+    _need(vcache, torch.bfloat16, 4, "vcache")
+    _need(out, torch.bfloat16, 3, "out")
+    B, H, L, d = kcache.shape
+    if vcache.shape != kcache.shape or tuple(q.shape) != (B, H, d) or tuple(out.shape) != (B, H, d):
+        raise ValueError("expected q, out (B, H, d) and caches (B, H, L, d)")
+    if not (isinstance(slopes_dev, torch.Tensor) and slopes_dev.device == q.device and
+            slopes_dev.dtype == torch.float32 and slopes_dev.is_contiguous() and slopes_dev.numel() == H):
+        raise ValueError("slopes_dev must be H contiguous fp32 values on q's device")
+    with torch.cuda.device(q.device):
+        st = load_library().alibi_attn_decode_noalloc(
+            _P(q.data_ptr()), _P(kcache.data_ptr()), _P(vcache.data_ptr()), _P(out.data_ptr()),
+            B, H, L, d, _P(slopes_dev.data_ptr()), _stream_handle(q.device))
+    _check("alibi_attn_decode_noalloc", st)
     return out
 
 

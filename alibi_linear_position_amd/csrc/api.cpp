@@ -272,6 +272,21 @@ int alibi_attn_decode(const void* q, const void* kcache, const void* vcache, voi
   return launch_decode_plan(q, kcache, vcache, out, B, H, L, d, slopes, ws, stream);
 }
 
+int alibi_attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, void* out, int B, int H,
+                              int L, int d, const float* slopes, hipStream_t stream) {
+  int st = check_decode(q, kcache, vcache, out, slopes, B, H, L, d);
+  if (st != ALIBI_OK) return st;
+  const size_t bytes = decode_ws_bytes(B, H, L, d);
+  float* ws = nullptr;
+  if (bytes > 0) {
+    size_t cap = 0;
+    st = hip_status(alibi::decode_scratch(&ws, &cap));
+    if (st != ALIBI_OK) return st;
+    if (bytes > cap) return ALIBI_ENOTSUP;
+  }
+  return launch_decode_plan(q, kcache, vcache, out, B, H, L, d, slopes, ws, stream);
+}
+
 size_t alibi_decode_ws_bytes(int B, int H, int L, int d) {
   if (B < 1 || H < 1 || L < 1 || d < 1 || L > kMaxLen || d > 256 || d % 8 != 0) return 0;
   return decode_ws_bytes(B, H, L, d);

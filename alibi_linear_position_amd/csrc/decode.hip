@@ -15,9 +15,22 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <mutex>
+
 namespace alibi {
 
 namespace {
+
+// Scratch for the decode variant that allocates nothing: the partial softmax
+// states of the split key ranges, B H S (d + 2) floats. decode_plan keeps
+// B H S below 4096 + B H (S > 1 only for B H < 4096), so 8191 (256 + 2) floats
+// hold every plan for d <= 256. One copy per device, alive until the process
+// ends; host code uses the address resolved per device below, never the name.
+constexpr size_t kScratchFloats = size_t(8191) * (256 + 2);
+static __device__ __align__(256) float scratch[kScratchFloats];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeUnroll = 8;
@@ -179,6 +192,24 @@ hipError_t launch_split(const void* q, const void* kc, const void* vc, void* out
 }
 
 }  // namespace
+
+hipError_t decode_scratch(float** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // this device's copy of the array, resolved once with the device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
+}
 
 void decode_plan(int B, int H, int L, int d, int* splits, int* chunk) {
   (void)d;

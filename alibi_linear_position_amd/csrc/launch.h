@@ -81,4 +81,8 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* ou
 // Number of splits and keys per split the decode launcher will use.
 void decode_plan(int B, int H, int L, int d, int* splits, int* chunk);
 
+// The current device's file-scope decode scratch (a device address) and its
+// size in bytes; resolved once per device. Allocates nothing.
+hipError_t decode_scratch(float** ptr, size_t* bytes);
+
 }  // namespace alibi

@@ -130,6 +130,23 @@ int alibi_attn_decode_ws(const void* q, const void* kcache, const void* vcache, 
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): it
+ * calls no allocating routine. Instead of a workspace it uses a fixed scratch
+ * array compiled into the library, one per device, of 8191 (256 + 2) fp32
+ * values (8.45 MB), which holds the partial states of every split the decode
+ * makes for d <= 256; each device keeps its copy until the process ends. Its
+ * address is looked up once per device, on the first call with that device
+ * current. Arguments and results as alibi_attn_decode. Every call on one
+ * device shares that device's scratch: calls whose work overlaps on one device
+ * (other streams, other threads) race and must be ordered by the caller. No
+ * part of the scratch needs to start at zero. ALIBI_ENOTSUP if a shape would
+ * need more scratch than the array holds; ALIBI_EHIP if the lookup fails.
+ */
+int alibi_attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, void* out,
+                              int B, int H, int L, int d, const float* slopes, hipStream_t stream);
+
+/*
  * TEST ONLY, not on the hot path: materialises the fp32 attention weights
  * w (B, H, N, N) of the fp32 forward, so the printed weight matrices of the
  * 4-head seed-42 example can be checked on the device. Masked weights are

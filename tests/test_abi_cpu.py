@@ -314,3 +314,28 @@ def test_ehip_without_a_gpu(lib):
     assert lib.alibi_attn_decode_ws(FAKE, FAKE, FAKE, FAKE, 1, 1, 300, 128, FAKE, FAKE, need, None) == -3
     assert _bwd(lib, d=128) == -3
     assert lib.alibi_release() == 0
+
+
+def test_decode_noalloc_validation(lib):
+    f = lib.alibi_attn_decode_noalloc
+    assert f(None, FAKE, FAKE, FAKE, 1, 1, 8, 128, FAKE, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 0, 128, FAKE, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 127, FAKE, None) == -2
+    assert f(FAKE, FAKE + 8, FAKE, FAKE, 1, 1, 8, 128, FAKE, None) == -1
+    if not _has_gpu():
+        # valid arguments reach the scratch lookup, the first HIP call
+        assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 100000, 128, FAKE, None) == -3
+
+
+def test_every_decode_plan_fits_the_static_scratch(lib):
+    # alibi_attn_decode_noalloc's scratch holds 8191 (256 + 2) floats; the plan
+    # keeps B H S < 4096 + B H and splits only when B H < 4096
+    cap = 8191 * (256 + 2) * 4
+    worst = 0
+    for bh in list(range(1, 64)) + [100, 255, 256, 1000, 2047, 2048, 3000, 4095, 4096, 5000]:
+        for L in (1, 255, 256, 257, 1000, 4096, 32768, 70000, 1 << 20, 1 << 24):
+            for d in (8, 64, 128, 256):
+                need = lib.alibi_decode_ws_bytes(1, bh, L, d)
+                assert need <= cap, (bh, L, d, need)
+                worst = max(worst, need)
+    assert worst > cap // 2  # the sweep reaches the large plans
