@@ -266,6 +266,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // with its bias offset m log2(e) (8 (r / 4) + r % 4) / c1, so tiles without
   // a mask need one fma per score to complete the linear bias. Variants keep
   // the plain content score (their bias is not linear in the key index).
+  // The clamp-only causal variant seeds the tiles that lie wholly inside the
+  // distance where the floor starts (its seed is rebuilt per tile, see below);
+  // with 4 waves (more staging registers per lane) those extra tile classes
+  // would spill, so there every clamp tile takes the per-score path.
+  constexpr bool SEED = VAR == 0 || (VAR == kVarClamp && CAUSAL && NW == 8);
   f32x16 cinit;
   const float c21 = c2 / c1;
 #pragma unroll
@@ -408,16 +413,48 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       return;
     }
 
+    // Clamp-only causal variant, per wave and open tile: 0 = every bias lies
+    // above the floor (the plain linear bias: seeded scores, as VAR = 0),
+    // 1 = every bias is floored (one constant), 2 = the floor starts inside
+    // the tile (per score). Only class 0 seeds the scores. The bias is linear
+    // in the distance, so its extremes over the tile sit at the two extreme
+    // distances (whatever the slope's sign).
+    int cls = 2;
+    if constexpr (SEED && VAR != 0) {
+      if (!MASKED) {
+        const float bf = -c2 * float(qw_last + delta - j0), bn = -c2 * float(qw0 + delta - (j0 + BN - 1));
+        if (fminf(bf, bn) >= var.clamp2) cls = 0;
+        else if (fmaxf(bf, bn) <= var.clamp2) cls = 1;
+      }
+    }
+
     // ---- S^T = K Q^T ----
     f32x16 s[KB];
-    lds_mfma_ring<KS * KB, 4>(
-        [&](int n) {
-          return *reinterpret_cast<const bf16x8*>(sK + (32 * (n % KB) + l32) * KPITCH + (16 * (n / KB) + 8 * hi) * 2);
-        },
-        [&](int n, const bf16x8& a) {
-          const int ks = n / KB, kb = n % KB;
-          s[kb] = mfma32(a, qf[ks], ks == 0 ? cinit : s[kb]);
-        });
+    auto qk = [&](const f32x16& c0) {
+      lds_mfma_ring<KS * KB, 4>(
+          [&](int n) {
+            return *reinterpret_cast<const bf16x8*>(sK + (32 * (n % KB) + l32) * KPITCH + (16 * (n / KB) + 8 * hi) * 2);
+          },
+          [&](int n, const bf16x8& a) {
+            const int ks = n / KB, kb = n % KB;
+            s[kb] = mfma32(a, qf[ks], ks == 0 ? c0 : s[kb]);
+          });
+    };
+    if constexpr (VAR == 0) {
+      qk(cinit);
+    } else if constexpr (SEED) {
+      // The seed of a clamp tile is built here from a value the compiler
+      // cannot hoist, so its 16 registers are live only until the first
+      // k-step; it is zero outside class 0.
+      float c21t = cls == 0 ? c21 : 0.0f;
+      asm volatile("" : "+v"(c21t));
+      f32x16 cs;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cs[r] = c21t * float(8 * (r >> 2) + (r & 3));
+      qk(cs);
+    } else {
+      qk(cinit);
+    }
 
     // ---- bias, mask, online softmax ----
     // Plain ALiBi: s = q.k + (c2 / c1)(8 (r / 4) + r % 4) and the exponent is
@@ -425,10 +462,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const float bt0 = c2 * float(j0 + 4 * hi - pi);
     const float bt1 = bt0 + 32.0f * c2;
     const float dpos = float(pi - j0 - 4 * hi);  // distance of register 0 of key block 0
+    u32x4 pf[PS];
+    // scale of s in the exponent: c1 where s is the (seeded) content score, 1
+    // where the per-score variant path has already turned s into the exponent
+    const float sc = (VAR == 0 || (SEED && cls != 2)) ? c1 : 1.0f;
     // p = exp2(s sc + bias_kb) packed to bf16 (the P^T B operand), with the
     // row sum taken from the same bf16 values.
-    u32x4 pf[PS];
-    const float sc = VAR == 0 ? c1 : 1.0f;
     // Keys after the query (RIGHT) carry -c2 (j - pi): relative to the seed
     // this is the bias of the mirrored key minus 2 c2 (8 (r / 4) + r % 4).
     auto exp_block = [&](float b0, float b1) {
@@ -469,7 +508,39 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       }
     };
     float lsum;
-    if (VAR == 0 && !MASKED) {
+    if constexpr (SEED && VAR != 0 && !MASKED) {
+      // Clamp-only open tiles, all three classes in one loop. They share one
+      // rescale site (with two, the compiler copies the accumulators between
+      // the paths on every tile): classes 0 and 1 exponentiate against the
+      // running maximum as the plain path does below and fall through to the
+      // rescale only when a lane leaves (0, kOptLimit]; class 2 turns s into
+      // the exponent per score and always takes it.
+      float a0 = cls == 1 ? var.clamp2 : bt0, a1 = cls == 1 ? var.clamp2 : bt1;
+      bool redo = true;
+      float mcand = kNegInf;
+      if (cls != 2) {
+        lsum = exp_block(a0 - m_run, a1 - m_run);
+        redo = __builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit)) != 0;
+        if (redo) mcand = max_xor32(fmaxf(fmaf(max16(s[0]), c1, a0), fmaf(max16(s[1]), c1, a1)));
+      } else {
+        float tmax = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = variant_t(s[kb][r], dpos - float(off));
+            tmax = fmaxf(tmax, s[kb][r]);
+          }
+        }
+        mcand = max_xor32(tmax);
+        a0 = a1 = 0.0f;
+      }
+      if (redo) {
+        rescale(mcand);
+        lsum = exp_block(a0 - m_run, a1 - m_run);
+      }
+    } else if (VAR == 0 && !MASKED) {
       // Every key is visible and tiles go from the diagonal outwards, so the
       // running maximum is almost always already above this tile's scores:
       // exponentiate against it directly. A lane whose partial row sum leaves

@@ -160,3 +160,29 @@ def test_bf16_all_mitigations_full_size_every_element(alibi):
             ref = oracle.variant_head_ref(q[b, h], k[b, h], v[b, h], s[h], True, -87.0, True, 50.0)[0]
             st.add(out[b, h], ref)
     st.finish()
+
+
+def test_bf16_clamp_full_size_every_element(alibi):
+    # the bias floor alone at the paper's c_clamp = -87 on the N = 4096, d = 128
+    # shape: with the standard slopes some heads reach the floor within a few
+    # hundred keys and some never do, so open tiles of all three kinds (wholly
+    # above the floor, wholly on it, crossing it) occur; every element of 16 heads
+    wl = W.FWD_B8_H16_N4096_D128
+    shape = (1, wl.H, wl.N, wl.d)
+    q, k, v = W.gaussian_qkv_bf16(shape, seed=wl.seed + 1)
+    s = oracle.slopes_ref(wl.H)
+    out = alibi.attn_fwd_ex(dev(q), dev(k), dev(v), torch.from_numpy(s), True, clamp=-87.0).cpu()
+    st = Bf16Stats("N4096 d128 clamp -87")
+    for h in range(wl.H):
+        ref = oracle.variant_head_ref(q[0, h], k[0, h], v[0, h], s[h], True, -87.0)[0]
+        st.add(out[0, h], ref)
+    st.finish()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_clamp_signed_slopes(alibi, fwd_waves, d):
+    # slopes of either sign (a negative slope raises the bias with distance, so
+    # the floor binds near the diagonal instead of far from it) and zero
+    s = np.array([-0.05, 0.3, -0.001, 0.0, 0.02, 1.5], dtype=np.float32)
+    out, ref = _bf16_case(alibi, (1, 6, 700, d), (1, 6, 700, d), s, True, -6.0, False, None, seed=17)
+    check_bf16(out, ref, f"clamp signed slopes d={d}")
