@@ -46,6 +46,7 @@ EXPORTS = {
     "alibi_slopes_recipe": [_I, _I, _I, _P],
     "alibi_debug_schedule": [_I, _I, _I, _P],
     "alibi_debug_fwd_waves": [_I],
+    "alibi_debug_fwd_split": [_I],
     "alibi_debug_stream_read": [_P, ctypes.c_longlong, _P, _I, _P],
     "alibi_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
     "alibi_status_string": [_I],

@@ -341,6 +341,12 @@ int alibi_debug_fwd_waves(int nw) {
   return ALIBI_OK;
 }
 
+int alibi_debug_fwd_split(int mode) {
+  if (mode < 0 || mode > 2) return ALIBI_EINVAL;
+  alibi::set_fwd_split(mode);
+  return ALIBI_OK;
+}
+
 const char* alibi_status_string(int status) {
   switch (status) {
     case ALIBI_OK: return "ALIBI_OK: success";

@@ -74,6 +74,34 @@ std::atomic<int>& waves_override() {
 // workgroup per CU) halve the K/V staging per query row and measure faster for
 // d = 128, while d = 64, soft capping (more VALU work per score) and grids of
 // fewer than two 8-wave workgroups per CU run better as two 4-wave workgroups.
+// Forced key-range split of the plain causal form: 0 = automatic, 1 = never,
+// 2 = always (ALIBI_FWD_SPLIT at load time, or set_fwd_split).
+std::atomic<int>& split_override() {
+  static std::atomic<int> w{[] {
+    const char* e = std::getenv("ALIBI_FWD_SPLIT");
+    const int n = e != nullptr ? std::atoi(e) : 0;
+    return (n == 1 || n == 2) ? n : 0;
+  }()};
+  return w;
+}
+
+// The split form (two key groups of 4 waves per 128 query rows) for the plain
+// causal form (with offsets, the log-sum-exp output or the exact skipping,
+// which therefore stays bit-identical to the call without it) on grids too
+// small for the heaviest block's walk to hide behind other work: at most
+// kSplitMaxWg of its workgroups, two per CU. Measured at d = 64 and 128: 12-19%
+// faster up to 512 workgroups (B8 H8 N1024 d64 21.5 vs 24.5 us, B1 H16 N4096
+// d128 84 vs 96 us), even at 768 and slower at 1024, where every SIMD already
+// has its two waves for the whole run.
+constexpr long long kSplitMaxWg = 512;
+bool fwd_split(const FwdArgs& a, int flags) {
+  if (!a.causal || flags != 0) return false;
+  const int o = split_override().load(std::memory_order_relaxed);
+  if (o != 0) return o == 2;
+  if (waves_override().load(std::memory_order_relaxed) != 0) return false;
+  return (long long)a.B * a.H * ((a.Nq + 127) / 128) <= kSplitMaxWg;
+}
+
 int fwd_waves(const FwdArgs& a, int flags) {
   const int o = waves_override().load(std::memory_order_relaxed);
   if (o != 0) return o;
@@ -217,14 +245,27 @@ constexpr float kDeadLog2 = 140.0f + kLazy;
 
 // EXT = false compiles the plain call (alibi_attn_fwd: no offsets, no
 // skipping, no log-sum-exp output) without those paths.
-template <int D, int NW, bool CAUSAL, int VAR, bool EXT>
+//
+// SPLIT = 2 (plain causal form, 8 waves) splits the key range of a query
+// block instead of its rows: the workgroup owns 4 x 32 query rows, waves 0-3
+// take the block's key tiles 0, 2, 4, ... counted from the diagonal and waves
+// 4-7 the tiles 1, 3, 5, ... for the same rows, each group staging its own
+// tiles; at the end the two partial softmax states of a row (running maximum
+// m, row sum l, unnormalised output O) are merged through LDS as
+// M = max(m0, m1), l = 2^(m0 - M) l0 + 2^(m1 - M) l1, O likewise (the
+// stable-softmax algebra of "When Attention Goes Blind", App. B.1-B.2). The
+// heaviest causal block then walks half as many tiles, which is what bounds
+// grids too small to fill the chip twice over.
+template <int D, int NW, bool CAUSAL, int VAR, bool EXT, int SPLIT = 1>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, int H, int Nq, int Nk, int nqb, int total,
     const float* __restrict__ slopes, float c1, FwdVariant var) {
-  constexpr int NT = NW * 64;
+  static_assert(SPLIT == 1 || (SPLIT == 2 && NW == 8 && CAUSAL && VAR == 0), "split: plain causal, 8 waves");
+  constexpr int NWG = NW / SPLIT;  // waves per key group
+  constexpr int NT = NWG * 64;     // threads staging one group's tiles
   constexpr int BN = 64;
-  constexpr int BM = NW * 32;
+  constexpr int BM = NWG * 32;
   constexpr int KS = D / 16;       // MFMA k-steps of Q K^T
   constexpr int KB = BN / 32;      // 32-key blocks per tile
   constexpr int DB = D / 32;       // 32-wide d blocks of O
@@ -233,12 +274,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   constexpr int VPITCH = BN * 2 + 16;
   constexpr int KBYTES = BN * KPITCH;
   constexpr int STAGE = KBYTES + D * VPITCH;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem_all[SPLIT * 2 * STAGE];
 
-  const int tid = threadIdx.x;
   // The wave index is uniform across the wave; say so, so that every per-wave
   // condition below compiles to a scalar branch instead of masked execution.
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int grp = SPLIT == 1 ? 0 : wave_all / NWG;  // key group
+  const int wave = wave_all - grp * NWG;             // wave within the group
+  const int tid = int(threadIdx.x) - grp * NT;       // thread within the group
+  unsigned char* const smem = smem_all + grp * 2 * STAGE;  // the group's two stages
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -309,7 +353,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     // through resources that start at the tile, so missing rows read as zero.
     // With no tile to visit (every query before every key) tile 0 is staged
     // and never read.
-    int first = ntiles - 1;
+    int first = ntiles - 1 - grp;
     if (!CAUSAL && Nk % BN == 0) {  // the order of the loops below
       const int x = q0 + delta + 1, nfull = Nk / BN;
       const int tl = x < BN ? -1 : min(x / BN - 1, nfull - 1);
@@ -335,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // and the bound only grows with the distance, so everything at or below a
   // wave's first dead tile is dead; the workgroup stops at the lowest tile any
   // of its waves still needs, and a wave skips its own dead tiles before that.
-  __shared__ int s_dead[NW];
+  __shared__ int s_dead[NWG];
   int t_dead_wave = -1, t_dead = -1;
   if (EXT && CAUSAL && VAR == 0 && var.knorm != nullptr && c2 > 0.0f) {
     float kmax = 0.0f;
@@ -361,11 +405,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) td = min(td, __shfl_xor(td, off, 64));
     t_dead_wave = max(__builtin_amdgcn_readfirstlane(td), -1);
-    if (lane == 0) s_dead[wave] = t_dead_wave;
+    if (lane == 0 && grp == 0) s_dead[wave] = t_dead_wave;  // wave w + 4 has the same rows
     __syncthreads();
     t_dead = s_dead[0];
 #pragma unroll
-    for (int w2 = 1; w2 < NW; ++w2) t_dead = min(t_dead, s_dead[w2]);
+    for (int w2 = 1; w2 < NWG; ++w2) t_dead = min(t_dead, s_dead[w2]);
   }
 
   // Exponent of one score (log2 units) for the variants, from the plain
@@ -612,9 +656,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   const int x = q0 + delta + 1;  // keys [0, x) are at or before every query of the block
   if (CAUSAL) {
     const int t_open = x < BN ? -1 : min(min(x / BN - 1, Nk / BN - 1), ntiles - 1);
-    int tile = ntiles - 1;
-    for (; tile > t_open; --tile) step(tile, tile - 1, Masked{});
-    for (; tile > t_dead; --tile) step(tile, tile - 1, Left{});
+    // With the key range split, group g takes every SPLIT-th tile from
+    // ntiles - 1 - g down to min(t_open, t_dead) + 1; group 1 has one tile
+    // fewer when that range has an odd length and meets group 0's last barrier
+    // without a tile.
+    int tile = ntiles - 1 - grp;
+    for (; tile > t_open; tile -= SPLIT) step(tile, tile - SPLIT, Masked{});
+    for (; tile > t_dead; tile -= SPLIT) step(tile, tile - SPLIT, Left{});
+    if (SPLIT == 2 && grp == 1 && ((ntiles - 1 - min(t_open, t_dead)) & 1)) __syncthreads();
   } else {
     // Without the mask: the tiles around the diagonal and a partial last tile
     // first (masked path), then the tiles wholly after the block's queries
@@ -630,6 +679,36 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     for (int t = mid_hi; t > tl; --t) step(t, t - 1 > tl ? t - 1 : after_mid, Masked{});
     for (int t = tr; t < nfull; ++t) step(t, t + 1 < nfull ? t + 1 : tl, Right{});
     for (int t = tl; t >= 0; --t) step(t, t - 1, Left{});
+  }
+
+  if constexpr (SPLIT == 2) {
+    // Merge the two key groups' states of each row: wave w + 4 hands its
+    // lanes' (m, l, O) to wave w, which owns the same rows in the same lane
+    // layout. A group that saw no key of a row has m = -inf and weighs 0.
+    constexpr int NV = 16 * DB + 2;  // floats per lane
+    static_assert(NWG * NV * 64 * 4 <= SPLIT * 2 * STAGE, "hand-over fits in the stages");
+    float* const xs = reinterpret_cast<float*>(smem_all) + wave * NV * 64 + lane;
+    __syncthreads();  // every wave is done with its stages
+    if (grp == 1) {
+      xs[0] = m_run;
+      xs[64] = l_run;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[(2 + 16 * db + r) * 64] = o[db][r];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xs[0], l1 = xs[64];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = m_run == kNegInf ? 0.0f : fast_exp2(m_run - mm);
+    const float a1 = m1 == kNegInf ? 0.0f : fast_exp2(m1 - mm);
+    l_run = fmaf(l_run, a0, l1 * a1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = fmaf(o[db][r], a0, xs[(2 + 16 * db + r) * 64] * a1);
+    m_run = mm;
   }
 
   // ---- epilogue: O / l -> bf16; a row that saw no key gives 0 ----
@@ -651,12 +730,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   }
 }
 
-template <int D, int NW, bool CAUSAL, int VAR, bool EXT>
+template <int D, int NW, bool CAUSAL, int VAR, bool EXT, int SPLIT = 1>
 hipError_t launch_cfg(const FwdArgs& a, float c1, const FwdVariant& var, hipStream_t stream) {
-  constexpr int BM = NW * 32;
+  constexpr int BM = NW / SPLIT * 32;
   const int nqb = (a.Nq + BM - 1) / BM;
   const long long total = (long long)a.B * a.H * nqb;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, CAUSAL, VAR, EXT>), dim3(unsigned(total)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, CAUSAL, VAR, EXT, SPLIT>), dim3(unsigned(total)), dim3(NW * 64), 0,
                      stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.out, a.H, a.Nq, a.Nk, nqb, int(total), a.slopes, c1, var);
   return hipGetLastError();
@@ -680,6 +759,10 @@ hipError_t launch_var_nw(const FwdArgs& a, int flags, bool ext, float c1, const 
 
 template <int D, bool CAUSAL>
 hipError_t launch_var(const FwdArgs& a, int flags, bool ext, float c1, const FwdVariant& var, hipStream_t s) {
+  if constexpr (CAUSAL) {
+    if (fwd_split(a, flags))
+      return ext ? launch_cfg<D, 8, true, 0, true, 2>(a, c1, var, s) : launch_cfg<D, 8, true, 0, false, 2>(a, c1, var, s);
+  }
   return fwd_waves(a, flags) == 4 ? launch_var_nw<D, CAUSAL, 4>(a, flags, ext, c1, var, s)
                                   : launch_var_nw<D, CAUSAL, 8>(a, flags, ext, c1, var, s);
 }
@@ -687,6 +770,7 @@ hipError_t launch_var(const FwdArgs& a, int flags, bool ext, float c1, const Fwd
 }  // namespace
 
 void set_fwd_waves(int nw) { waves_override().store(nw, std::memory_order_relaxed); }
+void set_fwd_split(int mode) { split_override().store(mode, std::memory_order_relaxed); }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hipStream_t stream) {
   FwdVariant var;

@@ -63,6 +63,9 @@ hipError_t launch_fwd_generic(const FwdArgs& a, const FwdOptions& opt, bool f32,
 // MFMA forward, bf16, d in {64, 128}.
 // Waves per forward workgroup: 0 = automatic (the default), 4 or 8 = forced.
 void set_fwd_waves(int nw);
+// Key-range split of the plain causal forward: 0 = automatic (the default),
+// 1 = never, 2 = always.
+void set_fwd_split(int mode);
 hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hipStream_t stream);
 
 // Largest key norm of each (b, h) of k (B, H, N, d) bf16, d in {64, 128}, as P

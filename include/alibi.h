@@ -299,6 +299,21 @@ int alibi_debug_fail_allocations(int count);
 int alibi_debug_fwd_waves(int nw);
 
 /*
+ * TEST AND TUNING ONLY: the key-range split of the plain causal bf16 forward
+ * (no mitigation; offsets, the log-sum-exp output and the exact skipping
+ * allowed), process-wide. 0 = automatic (the default: split when the split
+ * grid has at most 512 workgroups and no wave count is forced),
+ * 1 = never, 2 = always. The split form runs 8-wave workgroups over 128 query
+ * rows, waves 0-3 and 4-7 taking alternate key tiles of those rows and merging
+ * their partial softmax states (m, l, O) at the end (the stable-softmax algebra
+ * of "When Attention Goes Blind", App. B.1-B.2); its output differs from the
+ * unsplit form's by rounding only. The environment variable ALIBI_FWD_SPLIT=1|2,
+ * read once at load, sets the same override. Not synchronised with launches in
+ * flight on other threads. ALIBI_EINVAL for other values.
+ */
+int alibi_debug_fwd_split(int mode);
+
+/*
  * MEASUREMENT ONLY: a plain streaming read of `bytes` bytes of device memory
  * at `buf` (16-byte aligned, bytes a positive multiple of 16), the practical
  * HBM read ceiling against which the decode's bandwidth is read. Each of

@@ -32,6 +32,20 @@ def pytest_collection_modifyitems(config, items):
             it.add_marker(skip)
 
 
+@pytest.fixture(params=["nw4", "nw8", "split"])
+def fwd_form(request):
+    """Forces one form of the plain causal bf16 forward for one test: 4- or
+    8-wave workgroups over the whole key range, or the key-range split."""
+    import alibi_linear_position_amd as alibi
+    lib = alibi.load_library()
+    nw, split = {"nw4": (4, 1), "nw8": (8, 1), "split": (0, 2)}[request.param]
+    assert lib.alibi_debug_fwd_waves(nw) == 0
+    assert lib.alibi_debug_fwd_split(split) == 0
+    yield request.param
+    assert lib.alibi_debug_fwd_waves(0) == 0
+    assert lib.alibi_debug_fwd_split(0) == 0
+
+
 @pytest.fixture(params=[4, 8], ids=["nw4", "nw8"])
 def fwd_waves(request):
     """Forces 4- or 8-wave workgroups in the bf16 forward kernel for one test."""

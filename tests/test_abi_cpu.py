@@ -222,6 +222,15 @@ def test_fwd_waves_override_validation(lib):
     assert lib.alibi_debug_fwd_waves(0) == 0
 
 
+def test_fwd_split_override_validation(lib):
+    # host-only setter: 0 (automatic), 1 (never) and 2 (always) are accepted
+    for mode in (1, 2, 0):
+        assert lib.alibi_debug_fwd_split(mode) == 0
+    for mode in (-1, 3, 4, 8):
+        assert lib.alibi_debug_fwd_split(mode) == -1
+    assert lib.alibi_debug_fwd_split(0) == 0
+
+
 def test_stream_read_validation(lib):
     # host-side checks only: every bad argument is refused before any launch
     P = ctypes.c_void_p

@@ -79,7 +79,7 @@ FWD_SMALL = [
 
 
 @pytest.mark.parametrize("B,H,N,d,causal", FWD_SMALL)
-def test_fwd_bf16_small(alibi, fwd_waves, B, H, N, d, causal):
+def test_fwd_bf16_small(alibi, fwd_form, B, H, N, d, causal):
     q, k, v = W.gaussian_qkv_bf16((B, H, N, d), seed=7 + N + H)
     s = oracle.slopes_ref(H)
     ref = oracle.attn_ref(q, k, v, s, causal=causal)
@@ -104,7 +104,7 @@ def test_fwd_bf16_full_configs_every_element(alibi, wl):
     check_bf16(out, ref, wl.name)
 
 
-def test_fwd_causality_poison_bitwise(alibi, fwd_waves):
+def test_fwd_causality_poison_bitwise(alibi, fwd_form):
     B, H, N, d = 1, 4, 300, 128
     q, k, v = W.gaussian_qkv_bf16((B, H, N, d), seed=11)
     s = alibi.slopes(H)
@@ -169,7 +169,7 @@ def test_decode_equals_last_forward_row(alibi):
     assert diff <= 2 * BF16_TOL
 
 
-def test_fwd_far_key_dominates_rows(alibi, fwd_waves):
+def test_fwd_far_key_dominates_rows(alibi, fwd_form):
     # A key far behind the diagonal scores far above every nearer key (q_i . k_j
     # large), so an off-diagonal tile must raise the running maximum well past
     # what the diagonal set: the rare rescale-and-redo path of the kernel.

@@ -38,7 +38,7 @@ def _pair(alibi, q, k, v, s, **kw):
     (1, 8, 3000, 128, "wide"),      # ragged length
     (2, 4, 1000, 64, None),
 ])
-def test_skip_is_bit_exact(alibi, fwd_waves, B, H, N, d, recipe):
+def test_skip_is_bit_exact(alibi, fwd_form, B, H, N, d, recipe):
     q, k, v = (dev(x) for x in W.gaussian_qkv_bf16((B, H, N, d), seed=21))
     s = alibi.slopes(H) if recipe is None else alibi.slopes_recipe(recipe, H)
     a, b = _pair(alibi, q, k, v, s)
@@ -59,7 +59,7 @@ def test_skip_with_large_norms_is_bit_exact(alibi):
     assert torch.equal(a, b)
 
 
-def test_skip_with_offsets_is_bit_exact(alibi, fwd_waves):
+def test_skip_with_offsets_is_bit_exact(alibi, fwd_form):
     q, _, _ = W.gaussian_qkv_bf16((1, 8, 300, 128), seed=23)
     _, k, v = W.gaussian_qkv_bf16((1, 8, 2000, 128), seed=24)
     q, k, v = dev(q), dev(k), dev(v)

@@ -114,7 +114,7 @@ def test_bf16_paper_settings_with_recipes(alibi, recipe):
     (64, 64, 4096, 4096, True),  # both offsets shifted
 ])
 @pytest.mark.parametrize("d", [64, 128])
-def test_bf16_mfma_offsets(alibi, fwd_waves, Nq, Nk, qo, ko, causal, d):
+def test_bf16_mfma_offsets(alibi, fwd_form, Nq, Nk, qo, ko, causal, d):
     s = oracle.slopes_ref(2)
     out, ref = _bf16_case(alibi, (2, 2, Nq, d), (2, 2, Nk, d), s, causal, None, False, None, qo, ko)
     check_bf16(out, ref, f"mfma offsets {Nq},{Nk},{qo},{ko},{causal} d={d}")
