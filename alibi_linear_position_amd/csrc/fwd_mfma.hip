@@ -552,36 +552,35 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       }
     };
     float lsum;
-    if constexpr (SEED && VAR != 0 && !MASKED) {
-      // Clamp-only open tiles, all three classes in one loop. They share one
-      // rescale site (with two, the compiler copies the accumulators between
-      // the paths on every tile): classes 0 and 1 exponentiate against the
-      // running maximum as the plain path does below and fall through to the
-      // rescale only when a lane leaves (0, kOptLimit]; class 2 turns s into
-      // the exponent per score and always takes it.
-      float a0 = cls == 1 ? var.clamp2 : bt0, a1 = cls == 1 ? var.clamp2 : bt1;
-      bool redo = true;
-      float mcand = kNegInf;
-      if (cls != 2) {
-        lsum = exp_block(a0 - m_run, a1 - m_run);
-        redo = __builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit)) != 0;
-        if (redo) mcand = max_xor32(fmaxf(fmaf(max16(s[0]), c1, a0), fmaf(max16(s[1]), c1, a1)));
-      } else {
-        float tmax = kNegInf;
+    if constexpr (VAR != 0 && !MASKED) {
+      // Open tiles of the variants. Every key is visible and the tiles go
+      // from the diagonal outwards, so, as in the plain path below, the
+      // exponent is taken against the running maximum directly and the bound
+      // and the rescale follow only when a lane's partial row sum leaves
+      // (0, kOptLimit]: the row maximum of the tile is never formed otherwise.
+      // Clamp-only tiles of class 0 (seeded, linear bias) and 1 (content
+      // score, one constant bias) keep their scores; the others turn s into
+      // the exponent per score. One rescale site (with two, the compiler
+      // copies the accumulators between the paths on every tile).
+      float a0 = 0.0f, a1 = 0.0f;
+      bool per_score = true;
+      if constexpr (SEED) {
+        if (cls != 2) {
+          per_score = false;
+          a0 = cls == 1 ? var.clamp2 : bt0;
+          a1 = cls == 1 ? var.clamp2 : bt1;
+        }
+      }
+      if (per_score) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-            s[kb][r] = variant_t(s[kb][r], dpos - float(off));
-            tmax = fmaxf(tmax, s[kb][r]);
-          }
+          for (int r = 0; r < 16; ++r) s[kb][r] = variant_t(s[kb][r], dpos - float(32 * kb + 8 * (r >> 2) + (r & 3)));
         }
-        mcand = max_xor32(tmax);
-        a0 = a1 = 0.0f;
       }
-      if (redo) {
-        rescale(mcand);
+      lsum = exp_block(a0 - m_run, a1 - m_run);
+      if (__builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit))) {
+        rescale(max_xor32(fmaxf(fmaf(max16(s[0]), sc, a0), fmaf(max16(s[1]), sc, a1))));
         lsum = exp_block(a0 - m_run, a1 - m_run);
       }
     } else if (VAR == 0 && !MASKED) {
