@@ -47,6 +47,7 @@ EXPORTS = {
     "alibi_debug_schedule": [_I, _I, _I, _P],
     "alibi_debug_fwd_waves": [_I],
     "alibi_debug_fwd_split": [_I],
+    "alibi_debug_fwd_form": [_I, _I, _I, _I, _I, _I, _I, _I, _P],
     "alibi_debug_stream_read": [_P, ctypes.c_longlong, _P, _I, _P],
     "alibi_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
     "alibi_status_string": [_I],
@@ -305,6 +306,16 @@ def attn_decode_noalloc(q, kcache, vcache, slopes_dev, out):
             B, H, L, d, _P(slopes_dev.data_ptr()), _stream_handle(q.device))
     _check("alibi_attn_decode_noalloc", st)
     return out
+
+
+def fwd_form(B, H, Nq, Nk, d, causal=True, flags=0, delta=0):
+    """The form a bf16 forward call with these sizes launches (host only): 0 = the
+    generic kernel, 4 or 8 = MFMA waves per workgroup, 2 = the key-range split."""
+    form = ctypes.c_int(-1)
+    st = load_library().alibi_debug_fwd_form(int(B), int(H), int(Nq), int(Nk), int(d), int(bool(causal)),
+                                             int(flags), int(delta), ctypes.byref(form))
+    _check("alibi_debug_fwd_form", st)
+    return form.value
 
 
 def decode_ws_bytes(B, H, L, d):

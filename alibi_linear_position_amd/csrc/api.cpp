@@ -341,6 +341,23 @@ int alibi_debug_fwd_waves(int nw) {
   return ALIBI_OK;
 }
 
+int alibi_debug_fwd_form(int B, int H, int Nq, int Nk, int d, int causal, int flags, int delta, int* form) {
+  if (form == nullptr || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || (flags & ~15) != 0) return ALIBI_EINVAL;
+  if (d != 64 && d != 128) {
+    *form = 0;
+    return ALIBI_OK;
+  }
+  alibi::FwdArgs a{};
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.causal = causal != 0;
+  *form = alibi::fwd_mfma_form(a, flags, delta);
+  return ALIBI_OK;
+}
+
 int alibi_debug_fwd_split(int mode) {
   if (mode < 0 || mode > 2) return ALIBI_EINVAL;
   alibi::set_fwd_split(mode);

@@ -51,6 +51,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <type_traits>
@@ -87,19 +88,34 @@ std::atomic<int>& split_override() {
 
 // The split form (two key groups of 4 waves per 128 query rows) for the plain
 // causal form (with offsets, the log-sum-exp output or the exact skipping,
-// which therefore stays bit-identical to the call without it) on grids too
-// small for the heaviest block's walk to hide behind other work: at most
-// kSplitMaxWg of its workgroups, two per CU. Measured at d = 64 and 128: 12-19%
-// faster up to 512 workgroups (B8 H8 N1024 d64 21.5 vs 24.5 us, B1 H16 N4096
-// d128 84 vs 96 us), even at 768 and slower at 1024, where every SIMD already
-// has its two waves for the whole run.
-constexpr long long kSplitMaxWg = 512;
-bool fwd_split(const FwdArgs& a, int flags) {
+// which therefore stays bit-identical to the call without it), where the
+// heaviest query block's walk bounds the run. A tile-step model: unsplit,
+// 4-wave workgroups of 128 rows walk T_b tiles each, two per CU, so the run
+// takes about max(max_b T_b, sum_b T_b / 512) steps; split, one 8-wave
+// workgroup per CU walks ceil(T_b / 2), about max(max_b ceil(T_b / 2),
+// sum_b ceil(T_b / 2) / 256). Measured against that model (d = 64 and 128,
+// interleaved A/B), the split form pays for its second LDS stage set, its
+// merge and its two rounds of workgroups when the modelled ratio is below
+// ~0.7: B8 H8 N1024 d64 (0.56) 21.5 vs 24.2 us, B1 H16 N4096 d128 (0.52) 84
+// vs 96 us, B4 H12 N2048 d64 (0.80) even, a 512-row chunk against 4096 keys
+// (0.95) and B2 H16 N4096 d128 (1.0) 10-19% slower.
+bool fwd_split(const FwdArgs& a, int flags, int delta) {
   if (!a.causal || flags != 0) return false;
   const int o = split_override().load(std::memory_order_relaxed);
   if (o != 0) return o == 2;
   if (waves_override().load(std::memory_order_relaxed) != 0) return false;
-  return (long long)a.B * a.H * ((a.Nq + 127) / 128) <= kSplitMaxWg;
+  long long t_max = 0, t_sum = 0, h_sum = 0;
+  for (long long q0 = 0; q0 < a.Nq; q0 += 128) {
+    const long long kend = std::max(0LL, std::min<long long>(a.Nk, q0 + 128 + delta));
+    const long long t = (kend + 63) / 64;
+    t_max = std::max(t_max, t);
+    t_sum += t;
+    h_sum += (t + 1) / 2;
+  }
+  const double bh = double(a.B) * a.H;
+  const double unsplit = std::max(double(t_max), bh * double(t_sum) / 512.0);
+  const double split = std::max(double((t_max + 1) / 2), bh * double(h_sum) / 256.0);
+  return split < 0.7 * unsplit;
 }
 
 int fwd_waves(const FwdArgs& a, int flags) {
@@ -759,7 +775,7 @@ hipError_t launch_var_nw(const FwdArgs& a, int flags, bool ext, float c1, const 
 template <int D, bool CAUSAL>
 hipError_t launch_var(const FwdArgs& a, int flags, bool ext, float c1, const FwdVariant& var, hipStream_t s) {
   if constexpr (CAUSAL) {
-    if (fwd_split(a, flags))
+    if (fwd_split(a, flags, var.delta))
       return ext ? launch_cfg<D, 8, true, 0, true, 2>(a, c1, var, s) : launch_cfg<D, 8, true, 0, false, 2>(a, c1, var, s);
   }
   return fwd_waves(a, flags) == 4 ? launch_var_nw<D, CAUSAL, 4>(a, flags, ext, c1, var, s)
@@ -769,6 +785,11 @@ hipError_t launch_var(const FwdArgs& a, int flags, bool ext, float c1, const Fwd
 }  // namespace
 
 void set_fwd_waves(int nw) { waves_override().store(nw, std::memory_order_relaxed); }
+
+int fwd_mfma_form(const FwdArgs& a, int flags, int delta) {
+  if (fwd_split(a, flags & 7, delta)) return 2;
+  return fwd_waves(a, flags & 7);
+}
 void set_fwd_split(int mode) { split_override().store(mode, std::memory_order_relaxed); }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hipStream_t stream) {

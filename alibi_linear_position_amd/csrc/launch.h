@@ -66,6 +66,9 @@ void set_fwd_waves(int nw);
 // Key-range split of the plain causal forward: 0 = automatic (the default),
 // 1 = never, 2 = always.
 void set_fwd_split(int mode);
+// The form the MFMA forward launches for these arguments: 4 or 8 = waves per
+// workgroup over the whole key range, 2 = the key-range split (8 waves).
+int fwd_mfma_form(const FwdArgs& a, int flags, int delta);
 hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hipStream_t stream);
 
 // Largest key norm of each (b, h) of k (B, H, N, d) bf16, d in {64, 128}, as P

@@ -23,6 +23,11 @@ log-sum-exp; 2.5x the forward's flops: five GEMMs of the causal triangle). Their
 form: the causal triangle for the mitigations, N^2 without the mask, and the
 visible keys of the 512 rows for the prefill.
 
+"configs" reports the plain causal forward at the other configurations of the
+workload table (B8 H8 N1024 d64, B4 H12 N2048 d64, B1 H16 N16384 d128), each
+over back-to-back launches of the C entry point, with the form the library
+picks (alibi_debug_fwd_form: waves per workgroup, or the key-range split).
+
 The CPU baseline is the fp64 oracle itself, timed on this host's cores on a
 bounded sample (whole heads of the same forward, whole (b, h) pairs of the
 same decode), scaled to the same units.
@@ -238,9 +243,49 @@ def main():
         "cpu_baseline": None,
     }
     res["next"] = next_forms(alibi, qg, kg, vg, s_f, fw)
+    res["configs"] = config_rates(alibi, W, dev, (qg, kg, vg, s_f))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(q, k, v, kc, vc, qd, fw, dw)
     print(json.dumps(res), flush=True)
+
+
+def config_rates(alibi, W, dev, warm_args):
+    """The plain forward at the other configurations of the workload table, each
+    timed over back-to-back launches of the C entry point (HIP events), with the
+    form the library picks for it. The headline forward runs between them so the
+    clock stays up."""
+    import ctypes
+    import torch
+    lib = alibi.load_library()
+    P = ctypes.c_void_p
+    st = P(torch.cuda.current_stream(dev).cuda_stream)
+    res = {}
+    for wl, reps in ((W.FWD_B8_H8_N1024_D64, 400), (W.FWD_B4_H12_N2048_D64, 200), (W.FWD_B1_H16_N16384_D128, 20)):
+        q, k, v = (x.to(dev) for x in W.gaussian_qkv_bf16(wl.shape, seed=wl.seed))
+        out = torch.empty_like(q)
+        s = alibi.slopes(wl.H).to(dev)
+        args = (P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(out.data_ptr()), wl.B, wl.H, wl.N, wl.d,
+                P(s.data_ptr()), 1, st)
+        for _ in range(20):  # clock up
+            alibi.attn_fwd(*warm_args[:3], warm_args[3], causal=True)
+        for _ in range(10):
+            assert lib.alibi_attn_fwd(*args) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            lib.alibi_attn_fwd(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all()
+        ms = e0.elapsed_time(e1) / reps
+        flops = fwd_flops(wl.B, wl.H, wl.N, wl.d)
+        f = alibi.fwd_form(wl.B, wl.H, wl.N, wl.N, wl.d)
+        form = "key-range split, 8 waves" if f == 2 else f"{f} waves"
+        res[wl.name] = {"value": round(flops / ms / 1e9, 1), "unit": "TFLOP/s", "ms_per_launch": round(ms, 5),
+                        "frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "form": form,
+                        "launches": reps}
+        del q, k, v, out
+    return res
 
 
 def time_launches(fn, warmup=10, reps=10):

@@ -301,8 +301,10 @@ int alibi_debug_fwd_waves(int nw);
 /*
  * TEST AND TUNING ONLY: the key-range split of the plain causal bf16 forward
  * (no mitigation; offsets, the log-sum-exp output and the exact skipping
- * allowed), process-wide. 0 = automatic (the default: split when the split
- * grid has at most 512 workgroups and no wave count is forced),
+ * allowed), process-wide. 0 = automatic (the default, when no wave count is
+ * forced: split where a tile-step model of the run, the heaviest query
+ * block's walk against the total work per CU, says the split form takes under
+ * 0.7 of the unsplit time; alibi_debug_fwd_form reports the choice),
  * 1 = never, 2 = always. The split form runs 8-wave workgroups over 128 query
  * rows, waves 0-3 and 4-7 taking alternate key tiles of those rows and merging
  * their partial softmax states (m, l, O) at the end (the stable-softmax algebra
@@ -312,6 +314,16 @@ int alibi_debug_fwd_waves(int nw);
  * flight on other threads. ALIBI_EINVAL for other values.
  */
 int alibi_debug_fwd_split(int mode);
+
+/*
+ * TEST AND TUNING ONLY: the form a bf16 forward call with these sizes would
+ * launch, under the current overrides. flags: the ALIBI_* option bits; delta:
+ * q_offset - k_offset. *form: 0 = the generic kernel (d not 64 or 128), 4 or 8
+ * = MFMA kernel with that many waves per workgroup over the whole key range,
+ * 2 = the key-range split (8 waves). Host only. ALIBI_EINVAL for sizes < 1,
+ * unknown flags or a NULL form.
+ */
+int alibi_debug_fwd_form(int B, int H, int Nq, int Nk, int d, int causal, int flags, int delta, int* form);
 
 /*
  * MEASUREMENT ONLY: a plain streaming read of `bytes` bytes of device memory

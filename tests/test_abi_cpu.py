@@ -222,6 +222,41 @@ def test_fwd_waves_override_validation(lib):
     assert lib.alibi_debug_fwd_waves(0) == 0
 
 
+def test_fwd_form_choice():
+    # the automatic choice of the bf16 forward's form (host logic, no GPU):
+    # the key-range split where the heaviest causal block's walk bounds the run
+    import alibi_linear_position_amd as alibi
+    f = alibi.fwd_form
+    assert f(8, 8, 1024, 1024, 64) == 2            # B8 H8 N1024 d64
+    assert f(1, 16, 4096, 4096, 128) == 2          # one batch of the N = 4096 shape
+    assert f(2, 8, 1024, 1024, 128) == 2
+    assert f(4, 12, 2048, 2048, 64) == 4           # B4 H12 N2048 d64: the split would not pay
+    assert f(8, 16, 4096, 4096, 128) == 8          # the N = 4096 benchmark shape
+    assert f(1, 16, 16384, 16384, 128) == 8        # B1 H16 N16384 d128
+    assert f(2, 16, 4096, 4096, 128) == 8
+    assert f(8, 16, 512, 4096, 128, delta=3584) == 4   # a 512-row chunk against 4096 keys
+    assert f(8, 8, 1024, 1024, 64, causal=False) == 4  # no causal imbalance to split
+    assert f(8, 8, 1024, 1024, 64, flags=1) == 4       # mitigations keep the whole key range
+    assert f(8, 8, 1024, 1024, 64, flags=8) == 2       # skipping takes the same form as without it
+    assert f(1, 2, 100, 100, 96) == 0                  # generic kernel
+    lib = alibi.load_library()
+    try:
+        assert lib.alibi_debug_fwd_waves(8) == 0       # a forced wave count turns the split off
+        assert f(8, 8, 1024, 1024, 64) == 8
+        assert lib.alibi_debug_fwd_waves(0) == 0
+        assert lib.alibi_debug_fwd_split(2) == 0       # forced split for the plain causal form only
+        assert f(8, 16, 4096, 4096, 128) == 2 and f(8, 16, 4096, 4096, 128, flags=2) == 8
+        assert lib.alibi_debug_fwd_split(1) == 0
+        assert f(8, 8, 1024, 1024, 64) == 4
+    finally:
+        lib.alibi_debug_fwd_waves(0)
+        lib.alibi_debug_fwd_split(0)
+    with pytest.raises(alibi.AlibiError):
+        f(0, 8, 1024, 1024, 64)
+    with pytest.raises(alibi.AlibiError):
+        f(1, 8, 1024, 1024, 64, flags=16)
+
+
 def test_fwd_split_override_validation(lib):
     # host-only setter: 0 (automatic), 1 (never) and 2 (always) are accepted
     for mode in (1, 2, 0):
