@@ -64,14 +64,10 @@ def decode_bytes(B, H, L, d):
     return 2.0 * B * H * L * d * 2 + 2.0 * B * H * d * 2
 
 
-def fwd_waves(B, H, N, d):
-    """Waves per workgroup of the plain bf16 forward launch, as the library picks
-    them: ALIBI_FWD_NW when set to 4 or 8, else 8 for d = 128 when the grid has at
-    least 512 eight-wave workgroups, else 4."""
-    env = os.environ.get("ALIBI_FWD_NW")
-    if env in ("4", "8"):
-        return int(env)
-    return 8 if d == 128 and B * H * ((N + 255) // 256) >= 512 else 4
+def fwd_kernel_name(alibi, B, H, N, d):
+    """The forward instantiation the library launches for the plain causal call."""
+    f = alibi.fwd_form(B, H, N, N, d)
+    return f"fwd_mfma_kernel<{d},8,true,0,false,2>" if f == 2 else f"fwd_mfma_kernel<{d},{f},true,0,false,1>"
 
 
 def traffic_bytes(profile_md, sources, root=ROOT):
@@ -224,7 +220,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes("fwd_mfma_B8_H16_N4096_d128.md", ["fwd_mfma.hip", "device_common.h"]),
-                     "kernel": f"fwd_mfma_kernel<128,{fwd_waves(fw.B, fw.H, fw.N, fw.d)},true,0,false>",
+                     "kernel": fwd_kernel_name(alibi, fw.B, fw.H, fw.N, fw.d),
                      "ms_per_launch": round(t_fwd * 1e3, 4),
                      "per_launch": f"{flops:.4e} flop"},
         "decode": {"value": round(gbs, 1), "unit": "GB/s",

@@ -138,3 +138,46 @@ def test_backward_zero_slopes_match_torch(alibi):
     o.backward(do.float())
     for g, r, n in ((dq, qt.grad, "dq"), (dk, kt.grad, "dk"), (dv, vt.grad, "dv")):
         check_grad(g, r.double().numpy(), f"{n} zero slopes vs torch")
+
+
+def test_backward_is_deterministic(alibi):
+    # no atomics: two calls on the same inputs give the same bits
+    q, k, v, do = _inputs((2, 4, 777, 128), 37)
+    s = torch.from_numpy(oracle.slopes_ref(4))
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    out, lse = alibi.attn_fwd_train(qd, kd, vd, s, True)
+    g1 = alibi.attn_bwd(qd, kd, vd, out, dod, lse, s, True)
+    g2 = alibi.attn_bwd(qd, kd, vd, out, dod, lse, s, True)
+    torch.cuda.synchronize()
+    for a, b, n in zip(g1, g2, ("dq", "dk", "dv")):
+        assert torch.equal(a, b), n
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_causality_poison_bitwise(alibi, d):
+    # With dO = 0 on rows >= cut, no gradient of a position < cut can depend on
+    # q, k or v at positions >= cut (rows < cut see only keys < cut, and rows
+    # >= cut contribute dS = P (dP - D) = 0), and every gradient at >= cut is 0.
+    # Poisoning those positions must leave the first `cut` rows bit for bit.
+    B, H, N, cut = 1, 4, 700, 333
+    q, k, v, do = _inputs((B, H, N, d), 39)
+    do[:, :, cut:] = 0
+    s = torch.from_numpy(oracle.slopes_ref(H))
+
+    def grads(q, k, v):
+        qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+        out, lse = alibi.attn_fwd_train(qd, kd, vd, s, True)
+        g = alibi.attn_bwd(qd, kd, vd, out, dod, lse, s, True)
+        torch.cuda.synchronize()
+        return [x.cpu() for x in g]
+
+    g1 = grads(q, k, v)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[:, :, cut:] = (4.0 * q[:, :, cut:].float()).to(torch.bfloat16)
+    k2[:, :, cut:] = (30.0 * q[:, :, cut:].float()).to(torch.bfloat16)
+    v2[:, :, cut:] = 1e4
+    g2 = grads(q2, k2, v2)
+    for a, b, n in zip(g1, g2, ("dq", "dk", "dv")):
+        assert torch.equal(a[:, :, :cut], b[:, :, :cut]), n
+        assert torch.count_nonzero(b[:, :, cut:]) == 0, n
+        assert torch.isfinite(b.float()).all(), n
