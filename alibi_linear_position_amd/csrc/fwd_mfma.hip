@@ -150,6 +150,14 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Largest |a_r| of 16 accumulator values.
+__device__ __forceinline__ float absmax16(const f32x16& a) {
+  float m = fabsf(a[0]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, fabsf(a[r]));
+  return m;
+}
+
 // Maximum of 16 accumulator values as a shallow tree of 3-input maxima.
 __device__ __forceinline__ float max16(const f32x16& a) {
   const float m0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
@@ -247,6 +255,9 @@ struct FwdVariant {
   float clamp2;   // bias floor c_clamp log2(e)
   float cap_in;   // 2 log2(e) / (sqrt(d) z): exp2(s cap_in) = e^(2 A / z) for s = q.k
   float cap_out;  // z log2(e)
+  float cap_y;      // 1 / (sqrt(d) z): y = s cap_y = A / z
+  float cap_small;  // largest |s| with |y| <= 1/2
+  float cap_p[4];   // z log2(e) times the coefficients of tanh(y) / y in y^2 on |y| <= 1/2
   // Exact underflow skipping (plain causal form only): `parts` partial maxima
   // of the key norms of each (b, h), or null.
   const float* knorm;
@@ -430,9 +441,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
 
   // Exponent of one score (log2 units) for the variants, from the plain
   // content score s = q.k and the signed distance pi - j (an exact integer).
-  auto variant_t = [&](float s, float dist) {
+  // POLY (soft cap, tiles whose every |A| <= z / 2): z tanh(A / z) from a
+  // polynomial instead of an exponential and a reciprocal.
+  auto variant_t = [&](float s, float dist, auto poly_tag) {
+    constexpr bool POLY = decltype(poly_tag)::value;
     float a;
-    if constexpr ((VAR & kVarSoftcap) != 0) {
+    if constexpr ((VAR & kVarSoftcap) != 0 && POLY) {
+      const float y = s * var.cap_y;
+      const float u = y * y;
+      a = y * fmaf(fmaf(fmaf(var.cap_p[3], u, var.cap_p[2]), u, var.cap_p[1]), u, var.cap_p[0]);
+    } else if constexpr ((VAR & kVarSoftcap) != 0) {
       // z tanh(A / z) = z (1 - 2 / (e^(2 A / z) + 1)); saturates to +-z
       const float e2 = fast_exp2(s * var.cap_in);
       a = var.cap_out * fmaf(-2.0f, __builtin_amdgcn_rcpf(e2 + 1.0f), 1.0f);
@@ -588,11 +606,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
         }
       }
       if (per_score) {
+        auto per_score_t = [&](auto poly_tag) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+          for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][r] = variant_t(s[kb][r], dpos - float(32 * kb + 8 * (r >> 2) + (r & 3)));
+            for (int r = 0; r < 16; ++r)
+              s[kb][r] = variant_t(s[kb][r], dpos - float(32 * kb + 8 * (r >> 2) + (r & 3)), poly_tag);
+          }
+        };
+        bool poly = false;
+        if constexpr ((VAR & kVarSoftcap) != 0) {
+          // the polynomial soft cap when every content logit of the tile has
+          // |A| <= z / 2 (a NaN or infinity takes the exact form)
+          const float amax = fmaxf(absmax16(s[0]), absmax16(s[1]));
+          poly = __builtin_amdgcn_ballot_w64(!(amax <= var.cap_small)) == 0;
         }
+        if (poly)
+          per_score_t(std::true_type{});
+        else
+          per_score_t(std::false_type{});
       }
       lsum = exp_block(a0 - m_run, a1 - m_run);
       if (__builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit))) {
@@ -633,7 +665,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
               x = s[kb][r];
               if (!CAUSAL && j > pi) x -= 2.0f * c21 * float(j - pi);  // symmetric bias -m |i - j|
             } else {
-              x = variant_t(s[kb][r], dpos - float(off));
+              x = variant_t(s[kb][r], dpos - float(off), std::false_type{});
             }
             if (MASKED) x = (j < Nk && (!CAUSAL || j <= pi)) ? x : kNegInf;
             s[kb][r] = x;
@@ -799,6 +831,14 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hi
   const double z = opt.softcap > 0.0f ? double(opt.softcap) : 1.0;
   var.cap_in = float(2.0 * double(c1) / z);
   var.cap_out = float(z * 1.4426950408889634);
+  // tanh(y) / y ~ p0 + p1 y^2 + p2 y^4 + p3 y^6 on |y| <= 1/2: a weighted
+  // least-squares (Lawson) fit for the relative error, 5.4e-7 at most there
+  // (6.2e-7 evaluated in fp32); A / z = s / (sqrt(d) z) = s c1 / (z log2(e)).
+  const double ycoef = double(c1) / 1.4426950408889634 / z;
+  var.cap_y = float(ycoef);
+  var.cap_small = float(0.5 / ycoef * (1.0 - 1e-6));
+  const double pc[4] = {0.999999463558197, -0.33326318860054016, 0.1319030225276947, -0.0444023571908474};
+  for (int i = 0; i < 4; ++i) var.cap_p[i] = float(pc[i] * z * 1.4426950408889634);
   var.knorm = opt.knorm;
   var.parts = opt.knorm_parts;
   var.lse = opt.lse;
