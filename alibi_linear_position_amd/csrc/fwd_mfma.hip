@@ -407,6 +407,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // wave's first dead tile is dead; the workgroup stops at the lowest tile any
   // of its waves still needs, and a wave skips its own dead tiles before that.
   __shared__ int s_dead[NWG];
+  // Log-distance bias table of each wave's open tile: four copies of the
+  // strip bias(D) for the tile's 95 distances, copy a shifted by a entries
+  // so that every lane reads its four consecutive keys with one aligned
+  // 16-byte read; copies 132 floats apart so those reads hit distinct banks.
+  constexpr int kTabPitch = 132;
+  __shared__ __attribute__((aligned(16))) float ltab[(VAR & kVarLog) != 0 ? NW * 4 * kTabPitch : 4];
   int t_dead_wave = -1, t_dead = -1;
   if (EXT && CAUSAL && VAR == 0 && var.knorm != nullptr && c2 > 0.0f) {
     float kmax = 0.0f;
@@ -443,20 +449,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // content score s = q.k and the signed distance pi - j (an exact integer).
   // POLY (soft cap, tiles whose every |A| <= z / 2): z tanh(A / z) from a
   // polynomial instead of an exponential and a reciprocal.
-  auto variant_t = [&](float s, float dist, auto poly_tag) {
+  auto variant_a = [&](float s, auto poly_tag) {
     constexpr bool POLY = decltype(poly_tag)::value;
-    float a;
     if constexpr ((VAR & kVarSoftcap) != 0 && POLY) {
       const float y = s * var.cap_y;
       const float u = y * y;
-      a = y * fmaf(fmaf(fmaf(var.cap_p[3], u, var.cap_p[2]), u, var.cap_p[1]), u, var.cap_p[0]);
+      return y * fmaf(fmaf(fmaf(var.cap_p[3], u, var.cap_p[2]), u, var.cap_p[1]), u, var.cap_p[0]);
     } else if constexpr ((VAR & kVarSoftcap) != 0) {
       // z tanh(A / z) = z (1 - 2 / (e^(2 A / z) + 1)); saturates to +-z
       const float e2 = fast_exp2(s * var.cap_in);
-      a = var.cap_out * fmaf(-2.0f, __builtin_amdgcn_rcpf(e2 + 1.0f), 1.0f);
+      return var.cap_out * fmaf(-2.0f, __builtin_amdgcn_rcpf(e2 + 1.0f), 1.0f);
     } else {
-      a = s * c1;
+      return s * c1;
     }
+  };
+  auto variant_t = [&](float s, float dist, auto poly_tag) {
+    const float a = variant_a(s, poly_tag);
     const float dd = CAUSAL ? dist : fabsf(dist);
     float b;
     if constexpr ((VAR & kVarLog) != 0) {
@@ -607,11 +615,47 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       }
       if (per_score) {
         auto per_score_t = [&](auto poly_tag) {
+          if constexpr ((VAR & kVarLog) != 0 && !RIGHT) {
+            // Every distance of an open tile left of the queries is
+            // D = base + e - k >= 0 with base = qw0 + delta - j0 (>= 63 here),
+            // e = l32 - 4 hi in [-4, 31] and k = 32 kb + 8 (r / 4) + r % 4 in
+            // [0, 59]: 95 values from Dlow = base - 63. Lane l computes the
+            // bias of Dlow + l and Dlow + l + 64 once, writes them into the
+            // four copies, and reads back its 32 biases as 8 aligned 16-byte
+            // reads (same wave: LDS keeps the order of its accesses).
+            float* const tb = ltab + wave_all * (4 * kTabPitch);
+            const int dlow = qw0 + delta - j0 - 63;
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const int t = lane + 64 * h2;
+              float bv = -mh * __builtin_amdgcn_logf(float(dlow + t) + 1.0f);
+              if constexpr ((VAR & kVarClamp) != 0) bv = fmaxf(bv, var.clamp2);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              s[kb][r] = variant_t(s[kb][r], dpos - float(32 * kb + 8 * (r >> 2) + (r & 3)), poly_tag);
+              for (int a = 0; a < 4; ++a)
+                if (t >= a) tb[a * kTabPitch + t - a] = bv;
+            }
+            const int cls4 = l32 & 3, e = l32 - 4 * hi;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                // strip entries start .. start + 3 hold D_first - 3 .. D_first
+                const int start = e - 8 * g - 32 * kb + 60;
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(tb + cls4 * kTabPitch + start - cls4);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const int r = 4 * g + 3 - q;
+                  s[kb][r] = variant_a(s[kb][r], poly_tag) + bv[q];
+                }
+              }
+            }
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                s[kb][r] = variant_t(s[kb][r], dpos - float(32 * kb + 8 * (r >> 2) + (r & 3)), poly_tag);
+            }
           }
         };
         bool poly = false;
