@@ -287,8 +287,8 @@ int alibi_debug_fail_allocations(int count);
 
 /*
  * TEST AND TUNING ONLY: waves per workgroup of the bf16 MFMA forward kernel,
- * process-wide. 0 = automatic (the default: 8 for d = 128 without soft capping
- * when the grid has at least 512 eight-wave workgroups, else 4), 4 or 8 =
+ * process-wide. 0 = automatic (the default: 8 for d = 128 when the grid has at
+ * least 512 eight-wave workgroups, else 4), 4 or 8 =
  * forced for every later call. The two differ only by rounding: a row's tiles
  * are visited in the same order, but which of them take the exact or the
  * bounded running maximum depends on the block height. The environment variable

@@ -237,6 +237,7 @@ def test_fwd_form_choice():
     assert f(8, 16, 512, 4096, 128, delta=3584) == 4   # a 512-row chunk against 4096 keys
     assert f(8, 8, 1024, 1024, 64, causal=False) == 4  # no causal imbalance to split
     assert f(8, 8, 1024, 1024, 64, flags=1) == 4       # mitigations keep the whole key range
+    assert f(8, 16, 4096, 4096, 128, flags=7) == 8     # every mitigation form: 8 waves at d = 128
     assert f(8, 8, 1024, 1024, 64, flags=8) == 2       # skipping takes the same form as without it
     assert f(1, 2, 100, 100, 96) == 0                  # generic kernel
     lib = alibi.load_library()
