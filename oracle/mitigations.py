@@ -11,6 +11,9 @@ Encodings" (arXiv 2608.03994):
   A* = z tanh(A / z).
 * Sec. 4.3: the settings used there (c_clamp = -87, z = 50) and the slopes
   of the explicit recipe adapted to log distances, m_h = -tau / log(delta_h + 1).
+* Sec. 5.2 "Connection to Previous Work" and Sec. 5.3 "Recommendations for
+  Model Training": a hard sliding window as the alternative to clamping, which
+  lets the computation ignore the out-of-window entries.
 
 Readings (where the pages leave a step open):
 
@@ -25,6 +28,12 @@ Readings (where the pages leave a step open):
   not used.
 * Heads are ordered steepest first (delta_1 is the smallest distance), like the
   default geometric schedule.
+* The hard window of a head is a count of tokens, W_h: key j stays visible to
+  query i when 0 <= i - j < W_h (positions, causal form only), so W_h = 1
+  keeps the query's own key and W_h <= 0 none. This count reproduces Sec.
+  5.2's figure (a 124-token window in a 2048-token context leaves 88.3% of
+  the causal entries out). The pages fix no window per head, so W_h is an
+  argument; the natural choice is the head's blindness distance.
 * The order of operations per entry is the one the four equations imply:
   A = Q K^T / sqrt(d); A <- z tanh(A / z) if soft-capped; D = i - j (|i - j|
   without the causal mask); D <- log(D + 1) if log-scaled; B = -m D;
@@ -78,11 +87,13 @@ def slopes_recipe_ref(recipe: str, H: int, log_distance: bool = False) -> np.nda
 
 
 def variant_head_ref(q, k, v, m, causal=True, clamp=None, log_distance=False, softcap=None,
-                     q_pos0=0, k_pos0=0):
+                     q_pos0=0, k_pos0=0, window=None):
     """One head with any mix of the Sec. 3.4 mitigations; returns (out, weights) in fp64.
 
     q: (n_q, d), k: (n_k, d), v: (n_k, d_v). Query row r sits at position
     q_pos0 + r and key row c at k_pos0 + c. A row with no visible key gives 0.
+    window: the head's hard window of W tokens (Sec. 5.2-5.3; causal only): key
+    c stays visible to row r when 0 <= dist < W; None = no window.
     """
     q = _f64(q)
     k = _f64(k)
@@ -92,6 +103,10 @@ def variant_head_ref(q, k, v, m, causal=True, clamp=None, log_distance=False, so
         a = float(softcap) * np.tanh(a / float(softcap))
     dist = distance_ref(q.shape[0], k.shape[0], q_pos0, k_pos0)
     visible = dist >= 0 if causal else np.ones(dist.shape, dtype=bool)
+    if window is not None:
+        if not causal:
+            raise ValueError("the hard window is defined for the causal form only")
+        visible = visible & (dist < int(window))
     dd = np.abs(dist).astype(np.float64)   # equals i - j wherever a causal key is visible
     if log_distance:
         dd = np.log(dd + 1.0)
@@ -104,10 +119,11 @@ def variant_head_ref(q, k, v, m, causal=True, clamp=None, log_distance=False, so
 
 
 def variant_ref(q, k, v, slopes, causal=True, clamp=None, log_distance=False, softcap=None,
-                q_offset=0, k_offset=0, return_weights=False):
+                q_offset=0, k_offset=0, return_weights=False, windows=None):
     """Multi-head form of :func:`variant_head_ref`.
 
-    q: (B, H, n_q, d); k, v: (B, H, n_k, d). Returns out (B, H, n_q, d_v), fp64.
+    q: (B, H, n_q, d); k, v: (B, H, n_k, d). windows: None or H per-head hard
+    windows. Returns out (B, H, n_q, d_v), fp64.
     """
     q = _f64(q)
     k = _f64(k)
@@ -119,7 +135,8 @@ def variant_ref(q, k, v, slopes, causal=True, clamp=None, log_distance=False, so
     for b in range(B):
         for h in range(H):
             o, w = variant_head_ref(q[b, h], k[b, h], v[b, h], slopes[h], causal, clamp,
-                                    log_distance, softcap, q_offset, k_offset)
+                                    log_distance, softcap, q_offset, k_offset,
+                                    None if windows is None else int(windows[h]))
             out[b, h] = o
             if return_weights:
                 wts[b, h] = w
