@@ -60,14 +60,15 @@ EXPORTS = {
 _RESTYPES = {"alibi_status_string": ctypes.c_char_p, "alibi_decode_ws_bytes": ctypes.c_size_t}
 
 # mitigation bits of alibi_fwd_opts.flags and the slope recipes (include/alibi.h)
-CLAMP, LOG_DISTANCE, SOFTCAP, SKIP_UNDERFLOW = 1, 2, 4, 8
+CLAMP, LOG_DISTANCE, SOFTCAP, SKIP_UNDERFLOW, WINDOW = 1, 2, 4, 8, 16
 RECIPES = {"default": 0, "steep": 1, "safe": 2, "wide": 3, "explicit": 4}
 
 
 class FwdOpts(ctypes.Structure):
     """Mirror of struct alibi_fwd_opts."""
     _fields_ = [("flags", ctypes.c_int), ("clamp_min", ctypes.c_float), ("softcap", ctypes.c_float),
-                ("q_offset", ctypes.c_int), ("k_offset", ctypes.c_int), ("lse", ctypes.c_void_p)]
+                ("q_offset", ctypes.c_int), ("k_offset", ctypes.c_int), ("lse", ctypes.c_void_p),
+                ("window", ctypes.c_void_p)]
 
 
 _lib = None
@@ -185,8 +186,8 @@ def attn_fwd_f32(q, k, v, slopes=None, causal=True, out=None):
 
 
 def attn_fwd_ex(q, k, v, slopes=None, causal=True, clamp=None, log_distance=False, softcap=None,
-                q_offset=0, k_offset=0, skip_underflow=False, out=None, lse=None):
-    """Forward with mitigations and position offsets.
+                q_offset=0, k_offset=0, skip_underflow=False, out=None, lse=None, window=None):
+    """Forward with mitigations, position offsets and an optional hard window.
 
     q: (B, H, Nq, d); k, v: (B, H, Nk, d); bf16 (MFMA / generic kernel) or fp32
     (generic kernel), by q's dtype. clamp: bias floor or None; log_distance:
@@ -194,6 +195,8 @@ def attn_fwd_ex(q, k, v, slopes=None, causal=True, clamp=None, log_distance=Fals
     q_offset + r, key row c at k_offset + c. skip_underflow: exact skipping of
     key tiles whose weights all round to zero (bit-identical output). lse: an
     fp32 (B, H, Nq) device tensor that receives each row's log-sum-exp.
+    window: None or H per-head windows in tokens (causal, no mitigation): query
+    r sees key c when 0 <= pos(r) - pos(c) < window[h].
     """
     import torch
     dtype = q.dtype
@@ -222,6 +225,13 @@ def attn_fwd_ex(q, k, v, slopes=None, causal=True, clamp=None, log_distance=Fals
         if tuple(lse.shape) != (B, H, Nq):
             raise ValueError("lse must be (B, H, Nq)")
         o.lse = lse.data_ptr()
+    wt = None
+    if window is not None:
+        wt = torch.as_tensor(window, dtype=torch.int32).reshape(-1).to(q.device).contiguous()
+        if wt.numel() != H:
+            raise ValueError(f"expected {H} windows, got {wt.numel()}")
+        o.flags |= WINDOW
+        o.window = wt.data_ptr()
     entry = "alibi_attn_fwd_ex" if dtype == torch.bfloat16 else "alibi_attn_fwd_ex_f32"
     with torch.cuda.device(q.device):
         st = getattr(load_library(), entry)(

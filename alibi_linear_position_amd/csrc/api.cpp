@@ -57,7 +57,7 @@ int check_fwd(const void* q, const void* k, const void* v, const void* out, cons
   if (causal != 0 && causal != 1) return ALIBI_EINVAL;
   *opt = alibi::FwdOptions{};
   if (opts != nullptr) {
-    if ((opts->flags & ~(ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP | ALIBI_SKIP_UNDERFLOW)) != 0)
+    if ((opts->flags & ~(ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP | ALIBI_SKIP_UNDERFLOW | ALIBI_WINDOW)) != 0)
       return ALIBI_EINVAL;
     if ((opts->flags & ALIBI_CLAMP) && !std::isfinite(opts->clamp_min)) return ALIBI_EINVAL;
     if ((opts->flags & ALIBI_SOFTCAP) && !(std::isfinite(opts->softcap) && opts->softcap > 0.0f))
@@ -71,6 +71,12 @@ int check_fwd(const void* q, const void* k, const void* v, const void* out, cons
     opt->k_offset = opts->k_offset;
     if (opts->lse != nullptr && !aligned(opts->lse, 4)) return ALIBI_EINVAL;
     opt->lse = opts->lse;
+    if (opts->flags & ALIBI_WINDOW) {
+      if (opts->window == nullptr || !aligned(opts->window, 4)) return ALIBI_EINVAL;
+      if (!causal || (opts->flags & (ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP)) != 0)
+        return ALIBI_ENOTSUP;
+      opt->window = opts->window;
+    }
   }
   if ((long long)B * H * Nk > (1LL << 31) * 4) return ALIBI_ENOTSUP;
   return ALIBI_OK;

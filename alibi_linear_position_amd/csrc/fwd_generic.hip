@@ -37,6 +37,7 @@ struct GenParams {
   int delta;        // position of query row 0 minus position of key row 0
   float inv_sqrt_d;
   float* lse;       // optional row log-sum-exp output (natural log)
+  const int* window;  // optional per-head hard window of W tokens (causal): keys with 0 <= pi - j < W
 };
 
 template <typename T>
@@ -65,7 +66,12 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(
   }
   float m_run = kNegInf, l_run = 0.0f;
   const int jend = causal ? max(0, min(Nk, pi + 1)) : Nk;
-  for (int j = 0; j < jend; ++j) {
+  int jbeg = 0;
+  if (gp.window != nullptr) {  // keys j > pi - W ("When Attention Goes Blind", Sec. 5.2-5.3)
+    const long long jb = (long long)pi - gp.window[h] + 1;
+    jbeg = jb <= 0 ? 0 : (jb >= jend ? jend : int(jb));
+  }
+  for (int j = jbeg; j < jend; ++j) {
     float part = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -157,6 +163,7 @@ hipError_t launch_fwd_generic(const FwdArgs& a, const FwdOptions& opt, bool f32,
   gp.delta = opt.q_offset - opt.k_offset;
   gp.inv_sqrt_d = float(1.0 / std::sqrt(double(a.d)));
   gp.lse = opt.lse;
+  gp.window = opt.window;
   if (f32)
     hipLaunchKernelGGL(fwd_generic_kernel<float>, dim3(grid), dim3(256), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out,

@@ -265,6 +265,9 @@ struct FwdVariant {
   const float* knorm;
   int parts;
   float* lse;  // optional (B, H, Nq) row log-sum-exp output, natural log
+  // Optional hard window (plain causal form): H ints, query i sees key j when
+  // 0 <= pi - j < window[h] ("When Attention Goes Blind", Sec. 5.2-5.3).
+  const int* window;
 };
 
 // A score whose exponent lies more than this many log2 units below the row's
@@ -417,7 +420,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   constexpr int kTabPitch = 132;
   __shared__ __attribute__((aligned(16))) float ltab[(VAR & kVarLog) != 0 ? NW * 4 * kTabPitch : 4];
   int t_dead_wave = -1, t_dead = -1;
-  if (EXT && CAUSAL && VAR == 0 && var.knorm != nullptr && c2 > 0.0f) {
+  // Hard window: keys j <= pi - W are out of row i's window. Tiles up to
+  // t_wmask hold such a key for some row of the block and take the masked
+  // path; tiles wholly out of a wave's window are dead for it, like the
+  // skipped ones. W is clamped to +-2^30 so that pi - W stays an int.
+  const bool win_on = EXT && CAUSAL && VAR == 0 && var.window != nullptr;
+  const int wwin = win_on ? max(-(1 << 30), min(var.window[h], 1 << 30)) : (1 << 30);
+  int t_wmask = -1;
+  if (EXT && CAUSAL && VAR == 0 && ((var.knorm != nullptr && c2 > 0.0f) || win_on)) {
+    int td = -1;
+    if (var.knorm != nullptr && c2 > 0.0f) {
     float kmax = 0.0f;
     for (int p = 0; p < var.parts; ++p) kmax = fmaxf(kmax, var.knorm[(long long)bh * var.parts + p]);
     float qn2 = 0.0f;
@@ -435,7 +447,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const float reach_f = (kDeadLog2 + 2.0f * A) / c2 + 1.0f;
     const int reach = reach_f < 1.0e9f ? int(reach_f) + max(0, pi - Nk + 1) : (1 << 30);
     const int x = pi - reach;                                   // dead: j_max < x
-    int td = x >= 0 ? x / BN - 1 : -1;                           // last tile with j_max < x
+    td = x >= 0 ? x / BN - 1 : -1;                               // last tile with j_max < x
+    }
+    if (win_on) {
+      const int xw = pi - wwin + 1;                              // out of the window: j < xw
+      td = max(td, xw >= 0 ? xw / BN - 1 : -1);
+      const int xb = min(q0 + BM, Nq) - 1 + delta - wwin + 1;    // the same for the block's last row
+      t_wmask = xb >= 1 ? (xb - 1) / BN : -1;                    // tiles with j0 < xb
+    }
     if (i >= Nq) td = 1 << 30;                                   // rows past Nq do not count
     td = min(td, __shfl_xor(td, 32, 64));
 #pragma unroll
@@ -497,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const unsigned char* sV = sK + KBYTES;
     unsigned char* const sKn = smem + (stage ^ 1) * STAGE;
     stage ^= 1;
-    if ((MASKED && !(qw0 < Nq && (!CAUSAL || j0 <= qw_last + delta))) || (!MASKED && tile <= t_dead_wave)) {
+    if ((MASKED && !(qw0 < Nq && (!CAUSAL || j0 <= qw_last + delta))) || ((EXT || !MASKED) && tile <= t_dead_wave)) {
       regs.template store<KPITCH, VPITCH>(sKn, sKn + KBYTES, tid);
       return;
     }
@@ -714,7 +733,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
             } else {
               x = variant_t(s[kb][r], dpos - float(off), std::false_type{});
             }
-            if (MASKED) x = (j < Nk && (!CAUSAL || j <= pi)) ? x : kNegInf;
+            if (MASKED) x = (j < Nk && (!CAUSAL || j <= pi) && (!(EXT && CAUSAL && VAR == 0) || j > pi - wwin)) ? x : kNegInf;
             s[kb][r] = x;
             tmax = fmaxf(tmax, VAR == 0 ? fmaf(x, c1, kb ? bt1 : bt0) : x);
           }
@@ -756,7 +775,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     // without a tile.
     int tile = ntiles - 1 - grp;
     for (; tile > t_open; tile -= SPLIT) step(tile, tile - SPLIT, Masked{});
-    for (; tile > t_dead; tile -= SPLIT) step(tile, tile - SPLIT, Left{});
+    if constexpr (EXT && VAR == 0) {
+      // open tiles wholly inside every row's window, then the window's edge
+      const int t_lo = max(t_dead, t_wmask);
+      for (; tile > t_lo; tile -= SPLIT) step(tile, tile - SPLIT, Left{});
+      for (; tile > t_dead; tile -= SPLIT) step(tile, tile - SPLIT, Masked{});
+    } else {
+      for (; tile > t_dead; tile -= SPLIT) step(tile, tile - SPLIT, Left{});
+    }
     if (SPLIT == 2 && grp == 1 && ((ntiles - 1 - min(t_open, t_dead)) & 1)) __syncthreads();
   } else {
     // Without the mask: the tiles around the diagonal and a partial last tile
@@ -889,8 +915,9 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hi
   var.knorm = opt.knorm;
   var.parts = opt.knorm_parts;
   var.lse = opt.lse;
-  const int flags = opt.flags & 7;  // the mitigation bits; skipping is a run-time argument
-  const bool ext = var.delta != 0 || var.knorm != nullptr || var.lse != nullptr;
+  var.window = opt.window;
+  const int flags = opt.flags & 7;  // the mitigation bits; skipping and the window are run-time arguments
+  const bool ext = var.delta != 0 || var.knorm != nullptr || var.lse != nullptr || var.window != nullptr;
   if (a.d == 128)
     return a.causal ? launch_var<128, true>(a, flags, ext, c1, var, stream)
                     : launch_var<128, false>(a, flags, ext, c1, var, stream);

@@ -36,6 +36,9 @@ struct FwdOptions {
   int knorm_parts = 0;
   // optional output: row log-sum-exp of the logits (natural log), (B, H, Nq)
   float* lse = nullptr;
+  // optional per-head hard window (device, H ints; causal form only): query i
+  // sees key j when 0 <= pi - j < window[h]
+  const int* window = nullptr;
 };
 
 // One backward call (bf16 tensors (B, H, N, d), lse fp32 (B, H, N)).

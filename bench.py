@@ -16,7 +16,9 @@ inputs, each timed on its own (HIP events, after its own warmup): the Sec. 3.4
 mitigations of "When Attention Goes Blind" (bias floor -87, ln(D + 1)
 distances, soft cap 50; singly and all together), the symmetric non-causal
 bias, a chunked prefill (the last 512 query rows against the 4096-key
-cache through position offsets), and the exact underflow skipping (its rate
+cache through position offsets), hard per-head windows (Sec. 5.2-5.3; each
+head's window is where its bias reaches the fp32 denormal limit, rated on the
+in-window flops), and the exact underflow skipping (its rate
 counts the unskipped causal flops, so it is an effective rate, reported apart
 from the headline), and the backward pass (dq, dk, dv from the forward's
 log-sum-exp; 2.5x the forward's flops: five GEMMs of the causal triangle). Their flops are the algorithmic ones of each
@@ -44,6 +46,7 @@ short JSON line and no CPU baseline. The copy calibrates the HBM byte counters.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -322,6 +325,19 @@ def next_forms(alibi, q, k, v, s, fw):
                              "ms": round(ms, 4),
                              "note": "exact skipping of all-underflow key tiles; key-norm pass included; "
                                      "flops are the unskipped causal count, so this is not the headline"}
+    # hard per-head windows of "When Attention Goes Blind", Sec. 5.2-5.3: each
+    # head's window is the distance at which its bias alone reaches the fp32
+    # denormal limit, ceil(126 ln 2 / m_h) tokens (124 for the steepest head)
+    sl = s.detach().cpu().double().tolist()
+    wins = [min(N, int(math.ceil(126.0 * math.log(2.0) / m))) for m in sl]
+    wt = torch.tensor(wins, dtype=torch.int32, device=q.device)
+    ms = time_launches(lambda: alibi.attn_fwd_ex(q, k, v, s, True, out=out, window=wt))
+    vis = sum(sum(min(i + 1, w) for i in range(N)) for w in wins) * B
+    res["window_blindness"] = {"value": round(4.0 * d * vis / ms / 1e9, 1), "unit": "TFLOP/s (in-window flops)",
+                               "ms": round(ms, 4), "causal_equivalent": round(causal_flops / ms / 1e9, 1),
+                               "windows": wins,
+                               "note": "hard per-head windows (changes results: weights outside the window are "
+                                       "dropped); key tiles wholly out of a wave's window are skipped"}
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     alibi.attn_fwd_ex(q, k, v, s, True, out=out, lse=lse)
     dout = torch.randn(q.shape, generator=torch.Generator(device=q.device).manual_seed(7), device=q.device,

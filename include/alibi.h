@@ -184,6 +184,19 @@ int alibi_attn_weights_f32(const float* q, const float* k, float* w,
  * order them on one stream (or synchronise between them).
  */
 #define ALIBI_SKIP_UNDERFLOW 8
+/*
+ * ALIBI_WINDOW: a hard per-head sliding window ("When Attention Goes Blind",
+ * Sec. 5.2: steep heads already act as sliding windows, and Sec. 5.3: a hard
+ * window lets the computation ignore out-of-window entries instead of
+ * computing and discarding them). opts->window holds H ints on the device: a
+ * window of W tokens keeps key c for query r when 0 <= pos(r) - pos(c) < W,
+ * so W = 1 keeps the query's own key and W <= 0 none (a zero output row).
+ * This changes results wherever a weight falls outside the window. Key tiles
+ * wholly out of a wave's window are skipped. Causal form only
+ * (ALIBI_ENOTSUP with causal = 0) and without the mitigation bits
+ * (ALIBI_ENOTSUP); offsets, opts->lse and ALIBI_SKIP_UNDERFLOW combine with it.
+ */
+#define ALIBI_WINDOW 16
 
 typedef struct alibi_fwd_opts {
   int flags;         /* OR of the ALIBI_* bits above; other bits -> ALIBI_EINVAL */
@@ -194,6 +207,8 @@ typedef struct alibi_fwd_opts {
   float* lse;        /* optional device fp32 (B, H, Nq) output: each row's natural-log
                         log-sum-exp of its logits (-inf for a row that sees no key),
                         what alibi_attn_bwd needs; NULL = not written; 4-byte aligned */
+  const int* window; /* device, H ints: the per-head window in tokens; used with
+                        ALIBI_WINDOW (non-NULL, 4-byte aligned), ignored otherwise */
 } alibi_fwd_opts;
 
 /*

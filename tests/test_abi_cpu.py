@@ -179,7 +179,7 @@ def test_fwd_ex_validation(lib):
     assert _fwd_ex(lib, Nk=(1 << 24) + 1) == -1
     assert _fwd_ex(lib, k=None) == -1
     assert _fwd_ex(lib, causal=2) == -1
-    assert _fwd_ex(lib, opts=O(16, 0.0, 0.0, 0, 0)) == -1                # unknown flag bit
+    assert _fwd_ex(lib, opts=O(32, 0.0, 0.0, 0, 0)) == -1                # unknown flag bit
     assert _fwd_ex(lib, opts=O(1, float("nan"), 0.0, 0, 0)) == -1        # clamp not finite
     assert _fwd_ex(lib, opts=O(1, float("-inf"), 0.0, 0, 0)) == -1
     assert _fwd_ex(lib, opts=O(4, 0.0, 0.0, 0, 0)) == -1                 # soft cap must be > 0
@@ -191,7 +191,28 @@ def test_fwd_ex_validation(lib):
     assert _fwd_ex(lib, q=FAKE + 8) == -1
     assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", q=FAKE + 2, d=16) == -1
     assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", d=300) == -2
-    assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", opts=O(16, 0.0, 0.0, 0, 0), d=16) == -1
+    assert _fwd_ex(lib, "alibi_attn_fwd_ex_f32", opts=O(32, 0.0, 0.0, 0, 0), d=16) == -1
+
+
+def test_fwd_window_validation(lib):
+    # ALIBI_WINDOW (16): a non-NULL, 4-byte aligned per-head window array, the
+    # causal form only and no mitigation bits; checked before any HIP call
+    import alibi_linear_position_amd as alibi
+    O = alibi.FwdOpts
+    W = alibi.WINDOW
+    assert W == 16
+    for fn, d in (("alibi_attn_fwd_ex", 64), ("alibi_attn_fwd_ex_f32", 16)):
+        assert _fwd_ex(lib, fn, d=d, opts=O(W, 0.0, 0.0, 0, 0, None, None)) == -1          # no window array
+        assert _fwd_ex(lib, fn, d=d, opts=O(W, 0.0, 0.0, 0, 0, None, FAKE + 2)) == -1      # misaligned
+        assert _fwd_ex(lib, fn, d=d, causal=0, opts=O(W, 0.0, 0.0, 0, 0, None, FAKE)) == -2
+        for mit in (alibi.CLAMP, alibi.LOG_DISTANCE):
+            assert _fwd_ex(lib, fn, d=d, opts=O(W | mit, -87.0, 0.0, 0, 0, None, FAKE)) == -2
+        assert _fwd_ex(lib, fn, d=d, opts=O(W | alibi.SOFTCAP, 0.0, 50.0, 0, 0, None, FAKE)) == -2
+        # valid: validation passes and the first HIP call fails on this GPU-less box
+        assert _fwd_ex(lib, fn, d=d, opts=O(W, 0.0, 0.0, 3, 0, None, FAKE)) == -3
+        assert _fwd_ex(lib, fn, d=d, opts=O(W | alibi.SKIP_UNDERFLOW, 0.0, 0.0, 0, 0, None, FAKE)) == -3
+    # the window pointer is read only with the flag
+    assert _fwd_ex(lib, opts=O(0, 0.0, 0.0, 0, 0, None, FAKE + 2)) == -3
 
 
 @pytest.mark.parametrize("nbh", [1, 3, 7, 8, 12, 16, 24, 32, 40, 64, 128, 136, 512])
