@@ -15,6 +15,12 @@ The gradients below are the chain rule of that definition, step by step:
   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d)
 The bias is a constant, so it has no gradient of its own. The row log-sum-exp
 of the logits (natural log) is what a forward pass keeps for this backward.
+
+The paper trains its models with the Sec. 3.4 mitigations too. Two of them
+change only that constant bias and therefore only the logits here: the clamp,
+B* = max(B, c_clamp), and the log-scaled distance, B = -m log(D + 1) (the
+definitions of oracle.mitigations, with D = i - j under the mask and |i - j|
+without it). The soft cap, which changes the content logits, is not covered.
 """
 from __future__ import annotations
 
@@ -25,24 +31,34 @@ import numpy as np
 from .alibi_ref import _f64, bias_ref, distance_ref, softmax_rows_ref
 
 
-def _logits(q, k, m, causal):
+def _logits(q, k, m, causal, clamp=None, log_distance=False):
     a = (q @ k.T) / math.sqrt(q.shape[-1])
     dist = distance_ref(q.shape[0], k.shape[0])
-    logits = a + bias_ref(m, dist, causal)
+    if clamp is None and not log_distance:
+        bias = bias_ref(m, dist, causal)
+    else:
+        dd = np.abs(dist).astype(np.float64)
+        if log_distance:
+            dd = np.log(dd + 1.0)
+        bias = -float(m) * dd
+        if clamp is not None:
+            bias = np.maximum(bias, float(clamp))
+    logits = a + bias
     if causal:
         logits = np.where(dist < 0, -np.inf, logits)
     return logits
 
 
-def lse_head_ref(q, k, m, causal=True):
+def lse_head_ref(q, k, m, causal=True, clamp=None, log_distance=False):
     """Row log-sum-exp (natural log) of one head's logits, fp64."""
-    logits = _logits(_f64(q), _f64(k), m, causal)
+    logits = _logits(_f64(q), _f64(k), m, causal, clamp, log_distance)
     mx = np.max(logits, axis=-1, keepdims=True)
     return (mx + np.log(np.sum(np.exp(logits - mx), axis=-1, keepdims=True)))[:, 0]
 
 
-def attn_backward_head_ref(q, k, v, do, m, causal=True, magnitudes=False):
-    """(dq, dk, dv) of one head for the upstream gradient do, fp64.
+def attn_backward_head_ref(q, k, v, do, m, causal=True, magnitudes=False, clamp=None, log_distance=False):
+    """(dq, dk, dv) of one head for the upstream gradient do, fp64; clamp and
+    log_distance as in oracle.mitigations (a bias floor, ln(D + 1) distances).
 
     With ``magnitudes`` also the sums of absolute products behind each gradient
     element, (|dS| |K| / sqrt(d), |dS|^T |Q| / sqrt(d), P^T |dO|): the scale of
@@ -50,7 +66,7 @@ def attn_backward_head_ref(q, k, v, do, m, causal=True, magnitudes=False):
     the absolute value of its gradient).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    p = softmax_rows_ref(_logits(q, k, m, causal))
+    p = softmax_rows_ref(_logits(q, k, m, causal, clamp, log_distance))
     dv = p.T @ do
     dp = do @ v.T
     ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
@@ -62,7 +78,7 @@ def attn_backward_head_ref(q, k, v, do, m, causal=True, magnitudes=False):
     return grads, (a @ np.abs(k) * scale, a.T @ np.abs(q) * scale, p.T @ np.abs(do))
 
 
-def attn_backward_ref(q, k, v, do, slopes, causal=True):
+def attn_backward_ref(q, k, v, do, slopes, causal=True, clamp=None, log_distance=False):
     """Multi-head gradients: inputs (B, H, N, d); returns dq, dk, dv (B, H, N, d) fp64."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     slopes = np.asarray(_f64(slopes)).reshape(-1)
@@ -72,16 +88,17 @@ def attn_backward_ref(q, k, v, do, slopes, causal=True):
     for b in range(q.shape[0]):
         for h in range(q.shape[1]):
             dq[b, h], dk[b, h], dv[b, h] = attn_backward_head_ref(q[b, h], k[b, h], v[b, h], do[b, h],
-                                                                  slopes[h], causal)
+                                                                  slopes[h], causal, clamp=clamp,
+                                                                  log_distance=log_distance)
     return dq, dk, dv
 
 
-def lse_ref(q, k, slopes, causal=True):
+def lse_ref(q, k, slopes, causal=True, clamp=None, log_distance=False):
     """Row log-sum-exp (natural log), (B, H, N) fp64."""
     q, k = _f64(q), _f64(k)
     slopes = np.asarray(_f64(slopes)).reshape(-1)
     out = np.empty(q.shape[:3], dtype=np.float64)
     for b in range(q.shape[0]):
         for h in range(q.shape[1]):
-            out[b, h] = lse_head_ref(q[b, h], k[b, h], slopes[h], causal)
+            out[b, h] = lse_head_ref(q[b, h], k[b, h], slopes[h], causal, clamp, log_distance)
     return out

@@ -113,3 +113,65 @@ def test_backward_magnitudes_bound_the_gradients():
             assert np.array_equal(a, b)
     (_, _, dv), (_, _, mv) = oracle.attn_backward_head_ref(q, k, v, np.abs(do), 0.3, True, magnitudes=True)
     assert np.allclose(dv, mv, rtol=1e-13)
+
+
+# ---- the bias-only mitigations (clamp, log-scaled distance) in the backward ----
+
+def _torch_grads_bias(q, k, v, do, bias):
+    import torch
+    qt, kt, vt = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None],
+                                                           attn_mask=torch.tensor(bias))[0]
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("clamp,logd", [(-2.0, False), (None, True), (-1.5, True)])
+def test_backward_mitigations_match_autograd(causal, clamp, logd):
+    # autograd through SDPA with the mitigation's additive bias, whose values are
+    # the forward oracle's own (oracle.variant_head_ref's weights are pinned there)
+    n, d, m = 21, 16, 0.6
+    q, k, v, do = (_rand((n, d), s) for s in (31, 32, 33, 34))
+    _, w = oracle.variant_head_ref(q, k, v, m, causal, clamp, logd)
+    a = q @ k.T / math.sqrt(d)
+    lse = oracle.lse_head_ref(q, k, m, causal, clamp, logd)
+    # logits recovered from the pinned weights: log w + lse, -inf where w = 0 under the mask
+    with np.errstate(divide="ignore"):
+        logits = np.log(w) + lse[:, None]
+    bias = logits - a
+    got = oracle.attn_backward_head_ref(q, k, v, do, m, causal, clamp=clamp, log_distance=logd)
+    want = _torch_grads_bias(q, k, v, do, bias)
+    for g, x in zip(got, want):
+        assert np.allclose(g, x, atol=1e-11, rtol=1e-9)
+
+
+@pytest.mark.parametrize("clamp,logd", [(-2.0, False), (None, True), (-1.0, True)])
+def test_backward_mitigations_match_finite_differences(clamp, logd):
+    n, d, m, eps = 6, 4, 0.8, 1e-6
+    q, k, v, do = (_rand((n, d), s, 0.7) for s in (35, 36, 37, 38))
+    dq, dk, dv = oracle.attn_backward_head_ref(q, k, v, do, m, True, clamp=clamp, log_distance=logd)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.variant_head_ref(qq, kk, vv, m, True, clamp, logd)
+        return float(np.sum(o * do))
+
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            plus = [q.copy(), k.copy(), v.copy()]
+            minus = [q.copy(), k.copy(), v.copy()]
+            plus[which][idx] += eps
+            minus[which][idx] -= eps
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * eps)
+        assert np.allclose(grad, num, atol=1e-7), which
+
+
+def test_backward_clamp_above_every_bias_is_the_slope_free_head():
+    # a floor at 0 lifts every bias -m D <= 0 to 0: the gradients of m = 0
+    q, k, v, do = (_rand((15, 8), s) for s in (39, 40, 41, 42))
+    for causal in (True, False):
+        got = oracle.attn_backward_head_ref(q, k, v, do, 0.9, causal, clamp=0.0)
+        want = oracle.attn_backward_head_ref(q, k, v, do, 0.0, causal)
+        for g, x in zip(got, want):
+            assert np.allclose(g, x, atol=1e-13)
