@@ -50,6 +50,7 @@ EXPORTS = {
     "alibi_debug_fwd_form": [_I, _I, _I, _I, _I, _I, _I, _I, _P],
     "alibi_debug_stream_read": [_P, ctypes.c_longlong, _P, _I, _P],
     "alibi_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
+    "alibi_attn_bwd_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P],
     "alibi_status_string": [_I],
     "alibi_release": [],
     "alibi_decode_ws_bytes": [_I, _I, _I, _I],
@@ -251,8 +252,10 @@ def attn_fwd_train(q, k, v, slopes=None, causal=True):
     return out, lse
 
 
-def attn_bwd(q, k, v, out, dout, lse, slopes=None, causal=True):
-    """Gradients (dq, dk, dv), bf16 (B, H, N, d), of the plain forward."""
+def attn_bwd(q, k, v, out, dout, lse, slopes=None, causal=True, clamp=None, log_distance=False):
+    """Gradients (dq, dk, dv), bf16 (B, H, N, d), of the plain forward, or of the
+    forward with the clamp and/or log-distance bias (lse from attn_fwd_ex with
+    the same settings)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _need(t, torch.bfloat16, 4, n)
@@ -264,12 +267,18 @@ def attn_bwd(q, k, v, out, dout, lse, slopes=None, causal=True):
         raise ValueError("lse must be (B, H, N)")
     s = _slopes_dev(slopes, H, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    o = None
+    if clamp is not None or log_distance:
+        o = FwdOpts()
+        o.flags = (CLAMP if clamp is not None else 0) | (LOG_DISTANCE if log_distance else 0)
+        o.clamp_min = float(clamp) if clamp is not None else 0.0
     with torch.cuda.device(q.device):
-        st = load_library().alibi_attn_bwd(
+        st = load_library().alibi_attn_bwd_ex(
             _P(q.data_ptr()), _P(k.data_ptr()), _P(v.data_ptr()), _P(out.data_ptr()),
             _P(dout.data_ptr()), _P(lse.data_ptr()), _P(dq.data_ptr()), _P(dk.data_ptr()),
-            _P(dv.data_ptr()), B, H, N, d, _P(s.data_ptr()), int(bool(causal)), _stream_handle(q.device))
-    _check("alibi_attn_bwd", st)
+            _P(dv.data_ptr()), B, H, N, d, _P(s.data_ptr()), int(bool(causal)),
+            None if o is None else ctypes.byref(o), _stream_handle(q.device))
+    _check("alibi_attn_bwd_ex", st)
     return dq, dk, dv
 
 

@@ -220,15 +220,27 @@ int alibi_attn_fwd_ex_f32(const float* q, const float* k, const float* v, float*
   return hip_status(alibi::launch_fwd_generic(a, opt, true, stream));
 }
 
-int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                   const float* slopes, int causal, hipStream_t stream) {
+int alibi_attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                      const float* slopes, int causal, const alibi_fwd_opts* opts, hipStream_t stream) {
   int st = check_common(q, k, v, out, slopes, B, H, N, d, 16);
   if (st != ALIBI_OK) return st;
   st = check_common(dout, dq, dk, dv, slopes, B, H, N, d, 16);
   if (st != ALIBI_OK) return st;
   if (lse == nullptr || !aligned(lse, 4)) return ALIBI_EINVAL;
   if (causal != 0 && causal != 1) return ALIBI_EINVAL;
+  int flags = 0;
+  float clamp_min = 0.0f;
+  if (opts != nullptr) {
+    if ((opts->flags & ~(ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP | ALIBI_SKIP_UNDERFLOW | ALIBI_WINDOW)) != 0)
+      return ALIBI_EINVAL;
+    if ((opts->flags & ALIBI_CLAMP) && !std::isfinite(opts->clamp_min)) return ALIBI_EINVAL;
+    // the soft cap, the window and position offsets are forward-only forms
+    if ((opts->flags & (ALIBI_SOFTCAP | ALIBI_WINDOW)) != 0 || opts->q_offset != 0 || opts->k_offset != 0)
+      return ALIBI_ENOTSUP;
+    flags = opts->flags & (ALIBI_CLAMP | ALIBI_LOG_DISTANCE);
+    clamp_min = opts->clamp_min;
+  }
   if (d != 64 && d != 128) return ALIBI_ENOTSUP;
   float* ws = nullptr;
   {
@@ -236,9 +248,18 @@ int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out,
     st = workspace_get(kBwd, (size_t)2 * B * H * N * sizeof(float), &ws);
   }
   if (st != ALIBI_OK) return st;
-  if (log_enabled()) std::fprintf(stderr, "[alibi] bwd B=%d H=%d N=%d d=%d causal=%d\n", B, H, N, d, causal);
-  const alibi::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, slopes, causal};
+  if (log_enabled())
+    std::fprintf(stderr, "[alibi] bwd B=%d H=%d N=%d d=%d causal=%d flags=%d\n", B, H, N, d, causal, flags);
+  alibi::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, slopes, causal};
+  a.flags = flags;
+  a.clamp2 = clamp_min * 1.4426950408889634f;  // as the forward forms its floor (log2 units)
   return hip_status(alibi::launch_bwd(a, ws, scale_log2(d), stream));
+}
+
+int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   const float* slopes, int causal, hipStream_t stream) {
+  return alibi_attn_bwd_ex(q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, slopes, causal, nullptr, stream);
 }
 
 int alibi_slopes_recipe(int recipe, int H, int log_distance, float* slopes_out) {

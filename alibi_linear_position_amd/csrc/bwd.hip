@@ -28,6 +28,11 @@
 //   (64-key tiles need more registers than two waves per SIMD leave).
 // Scores are in log2 units (c1 = log2(e) / sqrt(d), c2 = m log2(e)); masked and
 // out-of-range entries get P = 0.
+//
+// VAR (bits 1: clamp, 2: log distance) recomputes P with the bias of those
+// Sec. 3.4 mitigations, B = max(-m D*, c), D* = D or ln(D + 1): both change
+// only the constant bias, so the rest of the chain rule is the same. The
+// scores are then not seeded and the bias is formed per score.
 #include "device_common.h"
 #include "launch.h"
 
@@ -37,6 +42,21 @@
 namespace alibi {
 
 namespace {
+
+constexpr int kBwdClamp = 1, kBwdLog = 2;
+
+// Bias of distance D >= 0 in log2 units for the VAR forms.
+template <int VAR>
+__device__ __forceinline__ float var_bias(float dd, float c2, float mh, float clamp2) {
+  float b;
+  if constexpr ((VAR & kBwdLog) != 0) {
+    b = -mh * __builtin_amdgcn_logf(dd + 1.0f);  // -m ln(D + 1) log2(e) = -m log2(D + 1)
+  } else {
+    b = -c2 * dd;
+  }
+  if constexpr ((VAR & kBwdClamp) != 0) b = fmaxf(b, clamp2);
+  return b;
+}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -152,12 +172,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 // accumulator set and one set of key rows, so two waves fit on every SIMD, and
 // the two roles' MFMA and VALU work overlap within a step instead of waiting
 // for each other.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int VAR>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int H, int N, int nkb, int total,
-    const float* __restrict__ slopes, float c1, float scale) {
+    const float* __restrict__ slopes, float c1, float scale, float clamp2) {
   constexpr int NT = 512, BK = 128, BQ = 32;
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
   using Tile = SwzTile<D>;             // Q / dO tiles: swizzled rows of 2 D bytes
@@ -175,7 +195,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int bh = wb.bh;
   const int kblk = wb.rank;  // low key blocks see the most queries: scheduled first
   const int h = bh % H;
-  const float c2 = slopes[h] * kLog2e;
+  const float mh = slopes[h];
+  const float c2 = mh * kLog2e;
   const float c21 = c2 / c1;
   const long long base = (long long)bh * N * D;
   const long long rbase = (long long)bh * N;
@@ -187,7 +208,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // with -c2 / c1 (8 (r / 4) + r % 4) leaves one fma for the bias.
   f32x16 cinit;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) cinit[r] = -c21 * float(8 * (r >> 2) + (r & 3));
+  for (int r = 0; r < 16; ++r) cinit[r] = VAR == 0 ? -c21 * float(8 * (r >> 2) + (r & 3)) : 0.0f;
   // per-lane byte offsets of the swizzled tile reads
   const int rb = Tile::row_base(lane), tb0 = Tile::tr_base(lane, 0), tb1 = Tile::tr_base(lane, 1);
 
@@ -251,11 +272,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
         const int i = q0 + 8 * g + 4 * hi + e;
-        float t = fmaf(s[r], c1, bj);
-        if (!OPEN && !full) {
-          if (!CAUSAL && j > i) t -= 2.0f * c2 * float(j - i);  // symmetric bias -m |i - j|
-          if (CAUSAL && j > i) t = -__builtin_huge_valf();
+        float t;
+        if constexpr (VAR == 0) {
+          t = fmaf(s[r], c1, bj);
+          if (!OPEN && !full && !CAUSAL && j > i) t -= 2.0f * c2 * float(j - i);  // symmetric bias -m |i - j|
+        } else {
+          t = fmaf(s[r], c1, var_bias<VAR>(float(CAUSAL ? max(i - j, 0) : abs(i - j)), c2, mh, clamp2));
         }
+        if (!OPEN && !full && CAUSAL && j > i) t = -__builtin_huge_valf();
         s[r] = fast_exp2(t - L[e]);
       }
     }
@@ -377,12 +401,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------- dQ --------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int VAR>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dq, int H, int N, int nqb, int total, const float* __restrict__ slopes,
-    float c1, float scale) {
+    float c1, float scale, float clamp2) {
   constexpr int NT = 256, BM = 128, BN = 32;
   constexpr int KS = D / 16, KB = BN / 32, DB = D / 32, PS = BN / 16, CPR = D / 8;
   using Tile = SwzTile<D>;              // K and V tiles: swizzled rows of 2 D bytes
@@ -399,7 +423,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int bh = wb.bh;
   const int qblk = nqb - 1 - wb.rank;  // high query blocks see the most keys: scheduled first
   const int h = bh % H;
-  const float c2 = slopes[h] * kLog2e;
+  const float mh = slopes[h];
+  const float c2 = mh * kLog2e;
   const float c21 = c2 / c1;
   const long long base = (long long)bh * N * D;
   const long long rbase = (long long)bh * N;
@@ -423,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const float Dr = i < N ? dsum[rbase + i] : 0.0f;
   f32x16 cinit;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) cinit[r] = c21 * float(8 * (r >> 2) + (r & 3));
+  for (int r = 0; r < 16; ++r) cinit[r] = VAR == 0 ? c21 * float(8 * (r >> 2) + (r & 3)) : 0.0f;
   const int rb = Tile::row_base(lane), tb0 = Tile::tr_base(lane, 0), tb1 = Tile::tr_base(lane, 1);
   f32x16 acc[DB];
 #pragma unroll
@@ -501,11 +526,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * half + e;
-            float t = fmaf(s[r], c1, bt0 + 32.0f * kb * c2);
-            if (!OPEN && !full) {
+            float t;
+            if constexpr (VAR == 0) {
+              t = fmaf(s[r], c1, bt0 + 32.0f * kb * c2);
+              if (!OPEN && !full) {
+                const int jj = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+                if (!CAUSAL && jj > i) t -= 2.0f * c2 * float(jj - i);
+                if (jj >= N || (CAUSAL && jj > i)) t = -__builtin_huge_valf();
+              }
+            } else {
               const int jj = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (!CAUSAL && jj > i) t -= 2.0f * c2 * float(jj - i);
-              if (jj >= N || (CAUSAL && jj > i)) t = -__builtin_huge_valf();
+              t = fmaf(s[r], c1, var_bias<VAR>(float(CAUSAL ? max(i - jj, 0) : abs(i - jj)), c2, mh, clamp2) - L);
+              if (!OPEN && !full && (jj >= N || (CAUSAL && jj > i))) t = -__builtin_huge_valf();
             }
             x[e] = fast_exp2(t) * dp[r];
           }
@@ -543,7 +575,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int VAR>
 hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, hipStream_t stream) {
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int RPB = 256 / (D / 8);
@@ -554,19 +586,33 @@ hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, 
   const float scale = float(1.0 / std::sqrt(double(D)));
   const int nkb = (a.N + 127) / 128;
   const long long tk = (long long)a.B * a.H * nkb;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(unsigned(tk)), dim3(512), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VAR>), dim3(unsigned(tk)), dim3(512), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
-                     nkb, int(tk), a.slopes, c1, scale);
+                     nkb, int(tk), a.slopes, c1, scale, a.clamp2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.N + 127) / 128;
   const long long tq = (long long)a.B * a.H * nqb;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(unsigned(tq)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VAR>), dim3(unsigned(tq)), dim3(256), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dq, a.H, a.N, nqb, int(tq),
-                     a.slopes, c1, scale);
+                     a.slopes, c1, scale, a.clamp2);
   return hipGetLastError();
+}
+
+}  // namespace
+
+namespace {
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_var(const BwdArgs& a, float* dsum, float* lse2, float c1, hipStream_t stream) {
+  switch (a.flags & 3) {
+    case 0: return launch_bwd_cfg<D, CAUSAL, 0>(a, dsum, lse2, c1, stream);
+    case 1: return launch_bwd_cfg<D, CAUSAL, 1>(a, dsum, lse2, c1, stream);
+    case 2: return launch_bwd_cfg<D, CAUSAL, 2>(a, dsum, lse2, c1, stream);
+    default: return launch_bwd_cfg<D, CAUSAL, 3>(a, dsum, lse2, c1, stream);
+  }
 }
 
 }  // namespace
@@ -575,10 +621,10 @@ hipError_t launch_bwd(const BwdArgs& a, float* ws, float c1, hipStream_t stream)
   float* dsum = ws;
   float* lse2 = ws + (long long)a.B * a.H * a.N;
   if (a.d == 128)
-    return a.causal ? launch_bwd_cfg<128, true>(a, dsum, lse2, c1, stream)
-                    : launch_bwd_cfg<128, false>(a, dsum, lse2, c1, stream);
-  return a.causal ? launch_bwd_cfg<64, true>(a, dsum, lse2, c1, stream)
-                  : launch_bwd_cfg<64, false>(a, dsum, lse2, c1, stream);
+    return a.causal ? launch_bwd_var<128, true>(a, dsum, lse2, c1, stream)
+                    : launch_bwd_var<128, false>(a, dsum, lse2, c1, stream);
+  return a.causal ? launch_bwd_var<64, true>(a, dsum, lse2, c1, stream)
+                  : launch_bwd_var<64, false>(a, dsum, lse2, c1, stream);
 }
 
 }  // namespace alibi

@@ -55,6 +55,8 @@ struct BwdArgs {
   int B, H, N, d;
   const float* slopes;
   int causal;
+  int flags = 0;         // ALIBI_CLAMP | ALIBI_LOG_DISTANCE: the bias-only mitigations
+  float clamp2 = 0.0f;   // bias floor in log2 units (ALIBI_CLAMP)
 };
 
 // Backward, d in {64, 128}; ws holds 2 B H N floats (D and lse in log2 units).

@@ -345,6 +345,14 @@ def next_forms(alibi, q, k, v, s, fw):
     ms = time_launches(lambda: alibi.attn_bwd(q, k, v, out, dout, lse, s, True), warmup=5, reps=10)
     res["backward"] = {"value": round(2.5 * causal_flops / ms / 1e9, 1), "unit": "TFLOP/s", "ms": round(ms, 4),
                        "note": "dq, dk, dv; flops = 5 causal GEMMs (S, dP, dV, dK, dQ) = 2.5x the forward's"}
+    lse2 = torch.empty_like(lse)
+    out2 = torch.empty_like(q)
+    alibi.attn_fwd_ex(q, k, v, s, True, out=out2, lse=lse2, clamp=-87.0, log_distance=True)
+    ms = time_launches(lambda: alibi.attn_bwd(q, k, v, out2, dout, lse2, s, True, clamp=-87.0, log_distance=True),
+                       warmup=5, reps=10)
+    res["backward_clamp+log"] = {"value": round(2.5 * causal_flops / ms / 1e9, 1), "unit": "TFLOP/s",
+                                 "ms": round(ms, 4),
+                                 "note": "the backward of the clamp (-87) with log-scaled distances; bias per score"}
     nq = 512
     qc = q[:, :, N - nq:].contiguous()
     oc = torch.empty_like(qc)

@@ -259,6 +259,23 @@ int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                    hipStream_t stream);
 
 /*
+ * Backward pass of the forward with the bias-only mitigations of Sec. 3.4 of
+ * "When Attention Goes Blind" (the paper trains with them): opts->flags may
+ * hold ALIBI_CLAMP (opts->clamp_min, finite) and ALIBI_LOG_DISTANCE, which
+ * change only the constant bias, B = max(-m D*, c) with D* = D or ln(D + 1),
+ * so the gradients follow the same chain rule with P recomputed under that
+ * bias. lse must come from alibi_attn_fwd_ex with the same opts. Everything
+ * else as alibi_attn_bwd (which is this call with opts = NULL).
+ * ALIBI_SOFTCAP, ALIBI_WINDOW and nonzero offsets: ALIBI_ENOTSUP (forward-only
+ * forms); ALIBI_SKIP_UNDERFLOW is ignored; unknown bits or a non-finite
+ * clamp: ALIBI_EINVAL.
+ */
+int alibi_attn_bwd_ex(const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      int B, int H, int N, int d, const float* slopes, int causal,
+                      const alibi_fwd_opts* opts, hipStream_t stream);
+
+/*
  * Slope recipes from target blindness distances (host only). A head whose bias
  * should reach the fp32 underflow limit ln 2^-126 at distance delta gets
  * m = 126 ln(2) / delta ("When Attention Goes Blind": Sec. 3.2 blindness

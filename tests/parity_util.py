@@ -11,6 +11,28 @@ import torch
 
 BF16_TOL = 1e-2
 F32_TOL = 1e-5
+U_BF16 = 2.0 ** -8  # unit roundoff of bf16: 8 significant bits, round to nearest even
+# The forward's row log-sum-exp: its running maximum plus the log of a row sum of
+# bf16-rounded weights, a sum of positive terms each within relative U_BF16, so
+# |err| <= ln(1 + 2^-8) = 3.90e-3 plus fp32 rounding.
+LSE_TOL = 4e-3
+
+
+def o_rounding_bound(p, o, q, k, do):
+    """Bound on what the bf16 rounding of the forward output O does to dq and dk.
+
+    The backward takes D_i = sum_c dO_ic O_ic from the stored bf16 output, so
+    |dD_i| <= U_BF16 sum_c |dO_ic| |O_ic|. D enters dS = P (dP - D) as the term
+    -P_ij dD_i, hence |delta dq_i| <= |dD_i| sum_j P_ij |K_j| / sqrt(d) and
+    |delta dk_j| <= sum_i P_ij |dD_i| |Q_i| / sqrt(d). Cancellation inside dS
+    does not shrink this term: where P is nearly one-hot (a steep head with
+    log-scaled distances) the true dS is tiny and this rounding dominates it.
+    All arguments are fp64 arrays of one head: p (n, n), o, q, k, do (n, d).
+    """
+    scale = 1.0 / np.sqrt(q.shape[-1])
+    dd = U_BF16 * np.sum(np.abs(do) * np.abs(o), axis=-1, keepdims=True)
+    pd = p * dd
+    return pd @ np.abs(k) * scale, pd.T @ np.abs(q) * scale
 
 
 def half_ulp_bf16(o):

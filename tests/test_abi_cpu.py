@@ -322,6 +322,32 @@ def test_bwd_validation(lib):
     assert _bwd(lib, d=256) == -2
 
 
+def test_bwd_ex_validation(lib):
+    # the backward with the bias-only mitigations: clamp and log distance are
+    # accepted (then the first HIP call fails on this GPU-less box), the
+    # forward-only forms are not supported, unknown bits are invalid
+    import alibi_linear_position_amd as alibi
+    O = alibi.FwdOpts
+
+    def bwd_ex(opts, **kw):
+        p = dict(d=64, causal=1)
+        p.update(kw)
+        return lib.alibi_attn_bwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, p["d"], FAKE,
+                                     p["causal"], None if opts is None else ctypes.byref(opts), None)
+
+    assert bwd_ex(None) == -3
+    for flags in (alibi.CLAMP, alibi.LOG_DISTANCE, alibi.CLAMP | alibi.LOG_DISTANCE,
+                  alibi.CLAMP | alibi.SKIP_UNDERFLOW):
+        assert bwd_ex(O(flags, -87.0, 0.0, 0, 0)) == -3, flags
+        assert bwd_ex(O(flags, -87.0, 0.0, 0, 0), causal=0, d=128) == -3, flags
+    assert bwd_ex(O(alibi.CLAMP, float("nan"), 0.0, 0, 0)) == -1          # clamp not finite
+    assert bwd_ex(O(64, 0.0, 0.0, 0, 0)) == -1                            # unknown bit
+    assert bwd_ex(O(alibi.SOFTCAP, 0.0, 50.0, 0, 0)) == -2                # forward-only forms
+    assert bwd_ex(O(alibi.WINDOW, 0.0, 0.0, 0, 0, None, FAKE)) == -2
+    assert bwd_ex(O(0, 0.0, 0.0, 5, 0)) == -2
+    assert bwd_ex(O(alibi.CLAMP, -87.0, 0.0, 0, 0), d=96) == -2
+
+
 def test_decode_ws_sizes_and_validation(lib):
     # c5 (B32 H32 L32768 d128): 4 key ranges per (b, h), (d + 2) fp32 states each
     assert lib.alibi_decode_ws_bytes(32, 32, 32768, 128) == 32 * 32 * 4 * 130 * 4

@@ -15,11 +15,9 @@ import torch
 
 import oracle
 import workloads as W
-from parity_util import Bf16Stats, F32_TOL, check_bf16, dev
+from parity_util import Bf16Stats, F32_TOL, LSE_TOL, check_bf16, dev
 
 pytestmark = pytest.mark.gpu
-
-LSE_TOL = 2.5e-3
 
 
 @pytest.fixture(scope="module")

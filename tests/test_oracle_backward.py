@@ -175,3 +175,36 @@ def test_backward_clamp_above_every_bias_is_the_slope_free_head():
         want = oracle.attn_backward_head_ref(q, k, v, do, 0.0, causal)
         for g, x in zip(got, want):
             assert np.allclose(g, x, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", ["steep_log", "plain"])
+def test_output_rounding_bound_covers_its_effect(case):
+    # The GPU gradient bar carries a term E for the forward's bf16 output: the
+    # backward forms D = rowsum(dO O) from the stored O. Here O is rounded to
+    # bf16 (torch's round-to-nearest-even) on the CPU and the chain rule redone
+    # in fp64 with that D: the change in dq and dk stays within E everywhere.
+    # The steep log-distance head (m = 14 on ln(D + 1), 300 tokens, d = 128) is
+    # where the rest of the bar alone is exceeded: P is nearly one-hot there.
+    import torch
+    import workloads as W
+    from parity_util import o_rounding_bound
+    if case == "steep_log":
+        q, k, v = (x[0, 1].double().numpy() for x in W.gaussian_qkv_bf16((1, 2, 300, 128), seed=61))
+        do = W.to_bf16_tensor(W.gaussian_f32((1, 2, 300, 128), 161))[0, 1].double().numpy()
+        m, logd = float(oracle.slopes_recipe_ref("steep", 2, True)[1]), True
+    else:
+        q, k, v, do = (_rand((200, 64), s) for s in (43, 44, 45, 46))
+        m, logd = 0.25, False
+    o, p = oracle.variant_head_ref(q, k, v, m, True, log_distance=logd)
+    (rq, rk, _), (mq, _, _) = oracle.attn_backward_head_ref(q, k, v, do, m, True, magnitudes=True,
+                                                            log_distance=logd)
+    ob = torch.from_numpy(o).to(torch.bfloat16).double().numpy()
+    scale = 1.0 / math.sqrt(q.shape[1])
+    ds = p * (do @ v.T - np.sum(do * ob, axis=-1, keepdims=True))
+    eq, ek = o_rounding_bound(p, o, q, k, do)
+    for got, ref, e in ((ds @ k * scale, rq, eq), (ds.T @ q * scale, rk, ek)):
+        err = np.abs(got - ref)
+        assert np.all(err <= e * (1 + 1e-9) + 1e-15)
+    if case == "steep_log":
+        err_q = np.abs(ds @ k * scale - rq)
+        assert np.any(err_q > 1e-2 + 1e-2 * (np.abs(rq) + mq))
