@@ -343,7 +343,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // a mask need one fma per score to complete the linear bias. Variants keep
   // the plain content score (their bias is not linear in the key index).
   // The clamp-only causal variant seeds the tiles that lie wholly inside the
-  // distance where the floor starts (its seed is rebuilt per tile, see below);
+  // distance where the floor starts and gives the others a zero C operand;
   // with 4 waves at d = 128 (more staging registers per lane) those extra
   // tile classes would spill, so there every clamp tile takes the per-score
   // path.
@@ -351,7 +351,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   f32x16 cinit;
   const float c21 = c2 / c1;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) cinit[r] = VAR == 0 ? c21 * float(8 * (r >> 2) + (r & 3)) : 0.0f;
+  for (int r = 0; r < 16; ++r) cinit[r] = SEED ? c21 * float(8 * (r >> 2) + (r & 3)) : 0.0f;
+  // Log-scaled distances without the soft cap: open tiles seed every score
+  // with -m_seed / c1, m_seed the row's running maximum (0 while it is
+  // -inf), so the per-score fma that adds the bias yields the exponent
+  // relative to the maximum directly. The seed is rebuilt where the maximum
+  // moves.
+  constexpr bool MSEED = (VAR & kVarLog) != 0 && (VAR & kVarSoftcap) == 0;
+  f32x16 mseed = f32x16{};
+  float m_seed = 0.0f;
+  const float rc1 = 1.0f / c1;
 
   // Q^T fragments (MFMA B operand): lane holds query l32, d = 16 ks + 8 hi .. +7.
   bf16x8 qf[KS];
@@ -415,8 +424,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   __shared__ int s_dead[NWG];
   // Log-distance bias table of each wave's open tile: four copies of the
   // strip bias(D) for the tile's 95 distances, copy a shifted by a entries
-  // so that every lane reads its four consecutive keys with one aligned
-  // 16-byte read; copies 132 floats apart so those reads hit distinct banks.
+  // (after 4 floats of padding, so that no write falls before its copy) so
+  // that every lane reads its four consecutive keys with one aligned 16-byte
+  // read; copies 132 floats apart so those reads hit distinct banks.
   constexpr int kTabPitch = 132;
   __shared__ __attribute__((aligned(16))) float ltab[(VAR & kVarLog) != 0 ? NW * 4 * kTabPitch : 4];
   int t_dead_wave = -1, t_dead = -1;
@@ -536,6 +546,27 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       }
     }
 
+    // Log-distance open tiles left of the queries: every distance of the tile
+    // is D = base + e - k >= 0 with base = qw0 + delta - j0 (>= 63 here),
+    // e = l32 - 4 hi in [-4, 31] and k = 32 kb + 8 (r / 4) + r % 4 in
+    // [0, 59]: 95 values from Dlow = base - 63. Lane l computes the bias of
+    // Dlow + l and Dlow + l + 64 once and writes them into the four copies
+    // before the Q K^T products, which hide the writes; the lanes read back
+    // their 32 biases as 8 aligned 16-byte reads afterwards (same wave: LDS
+    // keeps the order of its accesses).
+    if constexpr ((VAR & kVarLog) != 0 && KIND == 1) {
+      float* const tb = ltab + wave_all * (4 * kTabPitch);
+      const int dlow = qw0 + delta - j0 - 63;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int t = lane + 64 * h2;
+        float bv = -mh * __builtin_amdgcn_logf(float(dlow + t) + 1.0f);
+        if constexpr ((VAR & kVarClamp) != 0) bv = fmaxf(bv, var.clamp2);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) tb[a * kTabPitch + 4 + t - a] = bv;
+      }
+    }
+
     // ---- S^T = K Q^T ----
     f32x16 s[KB];
     auto qk = [&](const f32x16& c0) {
@@ -551,15 +582,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     if constexpr (VAR == 0) {
       qk(cinit);
     } else if constexpr (SEED) {
-      // The seed of a clamp tile is built here from a value the compiler
-      // cannot hoist, so its 16 registers are live only until the first
-      // k-step; it is zero outside class 0.
-      float c21t = cls == 0 ? c21 : 0.0f;
-      asm volatile("" : "+v"(c21t));
-      f32x16 cs;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cs[r] = c21t * float(8 * (r >> 2) + (r & 3));
-      qk(cs);
+      if (cls == 0)
+        qk(cinit);
+      else
+        qk(f32x16{});
+    } else if constexpr (MSEED && !MASKED) {
+      qk(mseed);
     } else {
       qk(cinit);
     }
@@ -578,7 +606,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     // row sum taken from the same bf16 values.
     // Keys after the query (RIGHT) carry -c2 (j - pi): relative to the seed
     // this is the bias of the mirrored key minus 2 c2 (8 (r / 4) + r % 4).
-    auto exp_block = [&](float b0, float b1) {
+    // NOADD: s already holds the exponent (the seeded log-distance tiles).
+    auto exp_block_t = [&](float b0, float b1, auto noadd_tag) {
+      constexpr bool NOADD = decltype(noadd_tag)::value;
       float lpart[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -594,7 +624,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
               bb0 = fmaf(-2.0f * c2, float(8 * (r0 >> 2) + (r0 & 3)), bb);
               bb1 = fmaf(-2.0f * c2, float(8 * (r0 >> 2) + (r0 & 3) + 1), bb);
             }
-            pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], sc, bb0)), fast_exp2(fmaf(s[kb][r0 + 1], sc, bb1)));
+            if constexpr (NOADD)
+              pk[e] = pack_bf16x2(fast_exp2(s[kb][r0]), fast_exp2(s[kb][r0 + 1]));
+            else
+              pk[e] = pack_bf16x2(fast_exp2(fmaf(s[kb][r0], sc, bb0)), fast_exp2(fmaf(s[kb][r0 + 1], sc, bb1)));
             lpart[e] = bdot2(pk[e], lpart[e]);
           }
           pf[2 * kb + half] = pk;
@@ -602,6 +635,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       }
       return (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
     };
+    auto exp_block = [&](float b0, float b1) { return exp_block_t(b0, b1, std::false_type{}); };
     // Lazy rescale: the running maximum moves only when a row's candidate
     // exceeds it by more than 2^kLazy.
     auto rescale = [&](float mcand) {
@@ -613,6 +647,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
         m_run = m_new;
+        if constexpr (MSEED) {
+          m_seed = m_run == kNegInf ? 0.0f : m_run;
+          const float sv = -m_seed * rc1;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mseed[r] = sv;
+        }
       }
     };
     float lsum;
@@ -638,24 +678,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       if (per_score) {
         auto per_score_t = [&](auto poly_tag) {
           if constexpr ((VAR & kVarLog) != 0 && !RIGHT) {
-            // Every distance of an open tile left of the queries is
-            // D = base + e - k >= 0 with base = qw0 + delta - j0 (>= 63 here),
-            // e = l32 - 4 hi in [-4, 31] and k = 32 kb + 8 (r / 4) + r % 4 in
-            // [0, 59]: 95 values from Dlow = base - 63. Lane l computes the
-            // bias of Dlow + l and Dlow + l + 64 once, writes them into the
-            // four copies, and reads back its 32 biases as 8 aligned 16-byte
-            // reads (same wave: LDS keeps the order of its accesses).
-            float* const tb = ltab + wave_all * (4 * kTabPitch);
-            const int dlow = qw0 + delta - j0 - 63;
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const int t = lane + 64 * h2;
-              float bv = -mh * __builtin_amdgcn_logf(float(dlow + t) + 1.0f);
-              if constexpr ((VAR & kVarClamp) != 0) bv = fmaxf(bv, var.clamp2);
-#pragma unroll
-              for (int a = 0; a < 4; ++a)
-                if (t >= a) tb[a * kTabPitch + t - a] = bv;
-            }
+            // the table written before the Q K^T products
+            const float* const tb = ltab + wave_all * (4 * kTabPitch);
             const int cls4 = l32 & 3, e = l32 - 4 * hi;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -663,7 +687,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
               for (int g = 0; g < 4; ++g) {
                 // strip entries start .. start + 3 hold D_first - 3 .. D_first
                 const int start = e - 8 * g - 32 * kb + 60;
-                const f32x4 bv = *reinterpret_cast<const f32x4*>(tb + cls4 * kTabPitch + start - cls4);
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(tb + cls4 * kTabPitch + 4 + start - cls4);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                   const int r = 4 * g + 3 - q;
@@ -692,10 +716,21 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
         else
           per_score_t(std::false_type{});
       }
-      lsum = exp_block(a0 - m_run, a1 - m_run);
-      if (__builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit))) {
-        rescale(max_xor32(fmaxf(fmaf(max16(s[0]), sc, a0), fmaf(max16(s[1]), sc, a1))));
+      if constexpr (MSEED) {
+        // s = t - m_seed: taken as it is; a row without a maximum yet (m_seed
+        // 0 stands in for it) goes through the bound like an overflow
+        lsum = exp_block_t(0.0f, 0.0f, std::true_type{});
+        if (__builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit) || m_run == kNegInf)) {
+          const float ms = m_seed;  // the seed s was built with
+          rescale(max_xor32(fmaxf(max16(s[0]), max16(s[1]))) + ms);
+          lsum = exp_block(ms - m_run, ms - m_run);
+        }
+      } else {
         lsum = exp_block(a0 - m_run, a1 - m_run);
+        if (__builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit))) {
+          rescale(max_xor32(fmaxf(fmaf(max16(s[0]), sc, a0), fmaf(max16(s[1]), sc, a1))));
+          lsum = exp_block(a0 - m_run, a1 - m_run);
+        }
       }
     } else if (VAR == 0 && !MASKED) {
       // Every key is visible and tiles go from the diagonal outwards, so the
