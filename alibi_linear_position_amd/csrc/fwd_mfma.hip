@@ -53,6 +53,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdlib>
 #include <type_traits>
 
@@ -257,9 +258,8 @@ struct FwdVariant {
   float clamp2;   // bias floor c_clamp log2(e)
   float cap_in;   // 2 log2(e) / (sqrt(d) z): exp2(s cap_in) = e^(2 A / z) for s = q.k
   float cap_out;  // z log2(e)
-  float cap_y;      // 1 / (sqrt(d) z): y = s cap_y = A / z
-  float cap_small;  // largest |s| with |y| <= 1/2
-  float cap_p[4];   // z log2(e) times the coefficients of tanh(y) / y in y^2 on |y| <= 1/2
+  float cap_small;  // largest |s| with |A| <= z / 4
+  float cap_q[3];   // z log2(e) tanh(A / z) ~ s (q0 + q1 s^2 + q2 s^4) for |A| <= z / 4
   // Exact underflow skipping (plain causal form only): `parts` partial maxima
   // of the key norms of each (b, h), or null.
   const float* knorm;
@@ -358,6 +358,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   // relative to the maximum directly. The seed is rebuilt where the maximum
   // moves.
   constexpr bool MSEED = (VAR & kVarLog) != 0 && (VAR & kVarSoftcap) == 0;
+  // Soft-capped open tiles build the exponent relative to the running
+  // maximum per score (the cap applies before the bias, so no seed can carry
+  // either); with MSEED, open tiles hand the exponentials t - m directly.
+  constexpr bool CAPREL = (VAR & kVarSoftcap) != 0;
+  constexpr bool REL = MSEED || CAPREL;
   f32x16 mseed = f32x16{};
   float m_seed = 0.0f;
   const float rc1 = 1.0f / c1;
@@ -479,20 +484,31 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
 
   // Exponent of one score (log2 units) for the variants, from the plain
   // content score s = q.k and the signed distance pi - j (an exact integer).
-  // POLY (soft cap, tiles whose every |A| <= z / 2): z tanh(A / z) from a
+  // POLY (soft cap, tiles whose every |A| <= z / 4): z tanh(A / z) from a
   // polynomial instead of an exponential and a reciprocal.
   auto variant_a = [&](float s, auto poly_tag) {
     constexpr bool POLY = decltype(poly_tag)::value;
     if constexpr ((VAR & kVarSoftcap) != 0 && POLY) {
-      const float y = s * var.cap_y;
-      const float u = y * y;
-      return y * fmaf(fmaf(fmaf(var.cap_p[3], u, var.cap_p[2]), u, var.cap_p[1]), u, var.cap_p[0]);
+      const float u = s * s;
+      return s * fmaf(fmaf(var.cap_q[2], u, var.cap_q[1]), u, var.cap_q[0]);
     } else if constexpr ((VAR & kVarSoftcap) != 0) {
       // z tanh(A / z) = z (1 - 2 / (e^(2 A / z) + 1)); saturates to +-z
       const float e2 = fast_exp2(s * var.cap_in);
       return var.cap_out * fmaf(-2.0f, __builtin_amdgcn_rcpf(e2 + 1.0f), 1.0f);
     } else {
       return s * c1;
+    }
+  };
+  // The soft-capped score plus B (the bias minus the row's reference
+  // maximum), the polynomial's last product fused with the addition.
+  auto variant_rel = [&](float s, float bb, auto poly_tag) {
+    constexpr bool POLY = decltype(poly_tag)::value;
+    if constexpr (POLY) {
+      const float u = s * s;
+      return fmaf(s, fmaf(fmaf(var.cap_q[2], u, var.cap_q[1]), u, var.cap_q[0]), bb);
+    } else {
+      const float e2 = fast_exp2(s * var.cap_in);
+      return fmaf(var.cap_out, fmaf(-2.0f, __builtin_amdgcn_rcpf(e2 + 1.0f), 1.0f), bb);
     }
   };
   auto variant_t = [&](float s, float dist, auto poly_tag) {
@@ -675,6 +691,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
           a1 = cls == 1 ? var.clamp2 : bt1;
         }
       }
+      // the maximum the per-score exponents of CAPREL tiles are taken against
+      // (0 for a row without one yet, which then takes the bound below)
+      const float mref = CAPREL ? (m_run == kNegInf ? 0.0f : m_run) : 0.0f;
       if (per_score) {
         auto per_score_t = [&](auto poly_tag) {
           if constexpr ((VAR & kVarLog) != 0 && !RIGHT) {
@@ -691,8 +710,38 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                   const int r = 4 * g + 3 - q;
-                  s[kb][r] = variant_a(s[kb][r], poly_tag) + bv[q];
+                  if constexpr (CAPREL)
+                    s[kb][r] = variant_rel(s[kb][r], bv[q] - mref, poly_tag);
+                  else
+                    s[kb][r] = variant_a(s[kb][r], poly_tag) + bv[q];
                 }
+              }
+            }
+          } else if constexpr (CAPREL && (VAR & kVarLog) != 0) {
+            // log-scaled distances right of the queries (no causal mask)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const float dd = fabsf(dpos - float(32 * kb + 8 * (r >> 2) + (r & 3)));
+                float bb = -mh * __builtin_amdgcn_logf(dd + 1.0f);
+                if constexpr ((VAR & kVarClamp) != 0) bb = fmaxf(bb, var.clamp2);
+                s[kb][r] = variant_rel(s[kb][r], bb - mref, poly_tag);
+              }
+            }
+          } else if constexpr (CAPREL) {
+            // linear bias -c2 |dpos - k| for key offset k: c2 (k - dpos) left
+            // of the queries, c2 (dpos - k) right of them (no causal mask)
+            const float sg = RIGHT ? -c2 : c2;
+            const float base = (RIGHT ? c2 : -c2) * dpos - mref;
+            const float floor_rel = var.clamp2 - mref;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                float bb = fmaf(sg, float(32 * kb + 8 * (r >> 2) + (r & 3)), base);
+                if constexpr ((VAR & kVarClamp) != 0) bb = fmaxf(bb, floor_rel);
+                s[kb][r] = variant_rel(s[kb][r], bb, poly_tag);
               }
             }
           } else {
@@ -707,7 +756,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
         bool poly = false;
         if constexpr ((VAR & kVarSoftcap) != 0) {
           // the polynomial soft cap when every content logit of the tile has
-          // |A| <= z / 2 (a NaN or infinity takes the exact form)
+          // |A| <= z / 4 (a NaN or infinity takes the exact form)
           const float amax = fmaxf(absmax16(s[0]), absmax16(s[1]));
           poly = __builtin_amdgcn_ballot_w64(!(amax <= var.cap_small)) == 0;
         }
@@ -716,12 +765,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
         else
           per_score_t(std::false_type{});
       }
-      if constexpr (MSEED) {
-        // s = t - m_seed: taken as it is; a row without a maximum yet (m_seed
-        // 0 stands in for it) goes through the bound like an overflow
+      if constexpr (REL) {
+        // s = t - m_ref (m_seed, or mref): taken as it is; a row without a
+        // maximum yet (0 stands in for it) goes through the bound like an
+        // overflow
+        const float ms = MSEED ? m_seed : mref;
         lsum = exp_block_t(0.0f, 0.0f, std::true_type{});
         if (__builtin_amdgcn_ballot_w64(!(lsum <= kOptLimit) || m_run == kNegInf)) {
-          const float ms = m_seed;  // the seed s was built with
           rescale(max_xor32(fmaxf(max16(s[0]), max16(s[1]))) + ms);
           lsum = exp_block(ms - m_run, ms - m_run);
         }
@@ -939,14 +989,15 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hi
   const double z = opt.softcap > 0.0f ? double(opt.softcap) : 1.0;
   var.cap_in = float(2.0 * double(c1) / z);
   var.cap_out = float(z * 1.4426950408889634);
-  // tanh(y) / y ~ p0 + p1 y^2 + p2 y^4 + p3 y^6 on |y| <= 1/2: a weighted
-  // least-squares (Lawson) fit for the relative error, 5.4e-7 at most there
-  // (6.2e-7 evaluated in fp32); A / z = s / (sqrt(d) z) = s c1 / (z log2(e)).
+  // tanh(y) / y ~ p0 + p1 y^2 + p2 y^4 on |y| <= 1/4: a weighted
+  // least-squares (Lawson) fit for the relative error, 4.0e-7 at most there
+  // (4.5e-7 evaluated in fp32); A / z = s / (sqrt(d) z) = s c1 / (z log2(e)).
+  // In s itself (y = s ycoef): z log2(e) tanh(y) = s sum_i q_i s^(2i) with
+  // q_i = z log2(e) p_i ycoef^(2i + 1).
   const double ycoef = double(c1) / 1.4426950408889634 / z;
-  var.cap_y = float(ycoef);
-  var.cap_small = float(0.5 / ycoef * (1.0 - 1e-6));
-  const double pc[4] = {0.999999463558197, -0.33326318860054016, 0.1319030225276947, -0.0444023571908474};
-  for (int i = 0; i < 4; ++i) var.cap_p[i] = float(pc[i] * z * 1.4426950408889634);
+  var.cap_small = float(0.25 / ycoef * (1.0 - 1e-6));
+  const double pc[3] = {0.9999996043367838, -0.3332190807322682, 0.1284161017710369};
+  for (int i = 0; i < 3; ++i) var.cap_q[i] = float(pc[i] * z * 1.4426950408889634 * std::pow(ycoef, 2 * i + 1));
   var.knorm = opt.knorm;
   var.parts = opt.knorm_parts;
   var.lse = opt.lse;
