@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libalibi.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "fwd_generic.hip", "fwd_mfma.hip", "decode.hip", "knorm.hip", "bwd.hip",
-           "stream_read.hip"]
+           "stream_read.hip", "mfma_rate.hip"]
 
 
 def hipcc() -> str:

@@ -9,7 +9,11 @@ One step = one pass over both hot-path kernels on resident inputs:
 diagonal, 4 d B H N (N+1) / 2, divided by the forward's own HIP-event time over
 the timed steps); the decode's GB/s (K + V + q + out bytes over its own event
 time) is reported under "decode". Both carry a roofline object against the
-MI355X datasheet peaks (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).
+MI355X datasheet peaks (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s). Beside
+the forward's peak, `roofline.mfma_ceiling` reports the matrix rate the part
+sustains (back-to-back register-fed bf16 MFMAs, measured in the same run): the
+shader clock drops under sustained matrix load, so this is below the datasheet
+figure, and the forward's fraction of it is reported too.
 
 After the timed steps, "next" reports the forward's other forms on the same
 inputs, each timed on its own (HIP events, after its own warmup): the Sec. 3.4
@@ -35,13 +39,14 @@ bounded sample (whole heads of the same forward, whole (b, h) pairs of the
 same decode), scaled to the same units.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --only fwd|decode|copy|bwd [--steps K] [--warmup W]
+    python bench.py --only fwd|decode|copy|bwd|mfma [--steps K] [--warmup W]
     python bench.py --only underflow     (CPU only: the bf16 underflow diagnostic
                                           of the 16384-token workload, fp64 oracle)
 
 `--only` runs a single kernel (`bwd`: the three backward kernels; `copy`: a
 plain device-to-device copy of
-a 1 GiB bf16 tensor) so that hardware-counter runs see one kernel; it prints a
+a 1 GiB bf16 tensor; `mfma`: the register-fed MFMA-rate kernel) so that
+hardware-counter runs see one kernel; it prints a
 short JSON line and no CPU baseline. The copy calibrates the HBM byte counters.
 """
 import argparse
@@ -142,8 +147,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd16k", "c1", "c2", "c3", "decode", "copy", "bwd", "oracle",
-                                       "underflow"], default=None)
+    ap.add_argument("--only", choices=["fwd", "fwd16k", "c1", "c2", "c3", "decode", "copy", "bwd", "mfma",
+                                       "oracle", "underflow"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -203,6 +208,7 @@ def main():
     gbs = nbytes / t_dec / 1e9
     assert torch.isfinite(out.float()).all() and torch.isfinite(od.float()).all()
     read_gbs = read_ceiling(alibi, (kc, vc), dev)
+    mfma_tflops = mfma_ceiling(alibi, dev, lambda: alibi.attn_decode(qd, kc, vc, s_d, out=od))
 
     res = {
         "metric": "causal ALiBi attn fwd TFLOP/s (bf16) + decode HBM GB/s, 1xMI355X",
@@ -225,7 +231,16 @@ def main():
                      "traffic": traffic_bytes("fwd_mfma_B8_H16_N4096_d128.md", ["fwd_mfma.hip", "device_common.h"]),
                      "kernel": fwd_kernel_name(alibi, fw.B, fw.H, fw.N, fw.d),
                      "ms_per_launch": round(t_fwd * 1e3, 4),
-                     "per_launch": f"{flops:.4e} flop"},
+                     "per_launch": f"{flops:.4e} flop",
+                     "mfma_ceiling": {"value": round(mfma_tflops, 1), "unit": "TFLOP/s",
+                                      "kernel": "mfma_rate_kernel",
+                                      "frac": round(tflops / mfma_tflops, 4),
+                                      "note": "back-to-back register-fed 32x32x16 bf16 MFMAs on every SIMD "
+                                              "(two waves per SIMD, random N(0,1) operands, no memory "
+                                              "traffic), timed in ~0.5 ms launches each followed by the "
+                                              "decode, as the forward runs in the step: the rate the part "
+                                              "sustains, below the datasheet peak because the shader clock "
+                                              "drops under sustained matrix load; context, not the peak"}},
         "decode": {"value": round(gbs, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -390,6 +405,40 @@ def read_ceiling(alibi, tensors, dev, workgroups=4096, warmup=2, steps=5):
     return nbytes * steps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def mfma_ceiling(alibi, dev, between, workgroups=1024, iters=160, warmup=5, steps=20):
+    """TFLOP/s of back-to-back register-fed bf16 MFMAs on every SIMD (two waves
+    per SIMD, random N(0, 1) operands like the forward's): the matrix rate the
+    part sustains, beside the forward's rate. Timed the way the benchmark step
+    runs the forward: launches of ~0.5 ms, each followed by `between` (the
+    decode), only the MFMA launches inside the events."""
+    import torch
+    lib = alibi.load_library()
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    frags = torch.randn(8 * 64 * 8, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    sink = torch.empty(8 * workgroups, dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def once():
+        rc = lib.alibi_debug_mfma_rate(frags.data_ptr(), iters, sink.data_ptr(), workgroups, st)
+        assert rc == 0, rc
+
+    for _ in range(warmup):
+        once()
+        between()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        once()
+        e1.record()
+        between()
+    torch.cuda.synchronize()
+    secs = sum(e0.elapsed_time(e1) for e0, e1 in ev) * 1e-3
+    flops = float(workgroups) * 8 * iters * 16 * 32768.0
+    return flops * steps / secs / 1e12
+
+
 def oracle_timing(W, dw, dev):
     """The fp64 oracle timed per configuration on this host's cores (a reported
     baseline, not the target): the tiny fp32 case and the two d = 64 forwards
@@ -542,6 +591,15 @@ def run_only(args, alibi, W, fw, dw, dev):
                            dtype=torch.float32).to(torch.bfloat16)
         fn = lambda: alibi.attn_bwd(q, k, v, out, dout, lse, s, True)
         work, unit = 2.5 * fwd_flops(fw.B, fw.H, fw.N, fw.d), "flop"
+    elif args.only == "mfma":
+        lib = alibi.load_library()
+        wgs, iters = 1024, 160
+        frags = torch.randn(8 * 64 * 8, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
+                            dtype=torch.float32).to(torch.bfloat16)
+        sink = torch.empty(8 * wgs, dtype=torch.float32, device=dev)
+        st = torch.cuda.current_stream().cuda_stream
+        fn = lambda: lib.alibi_debug_mfma_rate(frags.data_ptr(), iters, sink.data_ptr(), wgs, st)
+        work, unit = float(wgs) * 8 * iters * 16 * 32768.0, "flop"
     else:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
         dst = torch.empty_like(src)

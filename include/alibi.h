@@ -370,6 +370,24 @@ int alibi_debug_fwd_form(int B, int H, int Nq, int Nk, int d, int causal, int fl
 int alibi_debug_stream_read(const void* buf, long long bytes, unsigned* sink, int workgroups,
                             hipStream_t stream);
 
+/*
+ * MEASUREMENT ONLY: the sustained bf16 matrix rate of the part, against which
+ * the forward's MFMA rate is read beside the datasheet peak. Each of
+ * `workgroups` (1 .. 65536) workgroups of 8 waves (two per SIMD, as in the
+ * forward) runs, per wave, `iters` (1 .. 2^20) rounds of 16 back-to-back
+ * v_mfma_f32_32x32x16_bf16 from registers, over four independent accumulator
+ * chains; one round is 16 x 32768 flop per wave. `frags` (device memory,
+ * 16-byte aligned) holds the operand fragments as 8 x 64 lanes x 8 bf16: A_0 ..
+ * A_3 then B_0 .. B_3, lane l of A holding row l % 32, k = 8 (l / 32) .. + 7,
+ * and lane l of B column l % 32 at the same k; chain c accumulates A_c B_m for
+ * m = 0 .. 3 in turn. Wave w of workgroup g writes the sum of all its
+ * accumulator values, iters * sum_m sum(A_c B_m) summed over c, to
+ * sink[8 g + w] (device memory, 4-byte aligned, room for 8 workgroups fp32).
+ * Asynchronous on `stream`. ALIBI_EINVAL for bad arguments (checked before
+ * anything is enqueued).
+ */
+int alibi_debug_mfma_rate(const void* frags, int iters, float* sink, int workgroups, hipStream_t stream);
+
 /* Static, never-NULL description of a status code. */
 const char* alibi_status_string(int status);
 
