@@ -49,7 +49,7 @@ EXPORTS = {
     "alibi_debug_fwd_split": [_I],
     "alibi_debug_fwd_form": [_I, _I, _I, _I, _I, _I, _I, _I, _P],
     "alibi_debug_stream_read": [_P, ctypes.c_longlong, _P, _I, _P],
-    "alibi_debug_mfma_rate": [_P, _I, _P, _I, _P],
+    "alibi_debug_mfma_rate": [_P, _I, _I, _P, _I, _P],
     "alibi_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P],
     "alibi_attn_bwd_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P],
     "alibi_status_string": [_I],

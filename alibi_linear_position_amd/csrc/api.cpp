@@ -356,12 +356,13 @@ int alibi_debug_stream_read(const void* buf, long long bytes, unsigned* sink, in
   return hip_status(alibi::launch_stream_read(buf, bytes, sink, workgroups, stream));
 }
 
-int alibi_debug_mfma_rate(const void* frags, int iters, float* sink, int workgroups, hipStream_t stream) {
-  if (frags == nullptr || sink == nullptr || iters < 1 || iters > (1 << 20) || workgroups < 1 ||
-      workgroups > 65536 || (reinterpret_cast<uintptr_t>(frags) & 15u) != 0 ||
+int alibi_debug_mfma_rate(const void* frags, int iters, int valu, float* sink, int workgroups,
+                          hipStream_t stream) {
+  if (frags == nullptr || sink == nullptr || iters < 1 || iters > (1 << 20) || (valu != 0 && valu != 1) ||
+      workgroups < 1 || workgroups > 65536 || (reinterpret_cast<uintptr_t>(frags) & 15u) != 0 ||
       (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
     return ALIBI_EINVAL;
-  return hip_status(alibi::launch_mfma_rate(frags, iters, sink, workgroups, stream));
+  return hip_status(alibi::launch_mfma_rate(frags, iters, valu != 0, sink, workgroups, stream));
 }
 
 int alibi_debug_fail_allocations(int count) {

@@ -82,8 +82,10 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, const FwdOptions& opt, float c1, hi
 hipError_t launch_stream_read(const void* buf, long long bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 // Back-to-back register-fed bf16 MFMAs: 8-wave workgroups, each wave `iters`
 // rounds of 16 v_mfma_f32_32x32x16_bf16 on the 8 operand fragments at frags
-// (8 x 64 lanes x 16 bytes), its accumulator sum to sink[workgroup * 8 + wave].
-hipError_t launch_mfma_rate(const void* frags, int iters, float* sink, int workgroups, hipStream_t stream);
+// (8 x 64 lanes x 16 bytes), its accumulator sum to sink[workgroup * 8 + wave];
+// valu adds the forward's per-MFMA vector work beside every MFMA.
+hipError_t launch_mfma_rate(const void* frags, int iters, bool valu, float* sink, int workgroups,
+                            hipStream_t stream);
 hipError_t launch_knorm_max(const void* k, float* out, int B, int H, int N, int d, int P,
                             hipStream_t stream);
 

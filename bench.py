@@ -13,7 +13,9 @@ MI355X datasheet peaks (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s). Beside
 the forward's peak, `roofline.mfma_ceiling` reports the matrix rate the part
 sustains (back-to-back register-fed bf16 MFMAs, measured in the same run): the
 shader clock drops under sustained matrix load, so this is below the datasheet
-figure, and the forward's fraction of it is reported too.
+figure, and the forward's fraction of it is reported too;
+`roofline.mfma_valu_ceiling` adds the forward's per-MFMA softmax vector work to
+those MFMAs (the forward's instruction mix, without memory or stalls).
 
 After the timed steps, "next" reports the forward's other forms on the same
 inputs, each timed on its own (HIP events, after its own warmup): the Sec. 3.4
@@ -209,6 +211,7 @@ def main():
     assert torch.isfinite(out.float()).all() and torch.isfinite(od.float()).all()
     read_gbs = read_ceiling(alibi, (kc, vc), dev)
     mfma_tflops = mfma_ceiling(alibi, dev, lambda: alibi.attn_decode(qd, kc, vc, s_d, out=od))
+    mix_tflops = mfma_ceiling(alibi, dev, lambda: alibi.attn_decode(qd, kc, vc, s_d, out=od), valu=1)
 
     res = {
         "metric": "causal ALiBi attn fwd TFLOP/s (bf16) + decode HBM GB/s, 1xMI355X",
@@ -240,7 +243,15 @@ def main():
                                               "traffic), timed in ~0.5 ms launches each followed by the "
                                               "decode, as the forward runs in the step: the rate the part "
                                               "sustains, below the datasheet peak because the shader clock "
-                                              "drops under sustained matrix load; context, not the peak"}},
+                                              "drops under sustained matrix load; context, not the peak"},
+                     "mfma_valu_ceiling": {"value": round(mix_tflops, 1), "unit": "TFLOP/s",
+                                           "kernel": "mfma_rate_kernel (valu)",
+                                           "frac": round(tflops / mix_tflops, 4),
+                                           "note": "the same MFMAs, each joined by the vector work the "
+                                                   "forward's softmax issues per MFMA (fma, exponential, half "
+                                                   "a bf16 pack, half a bf16 dot, an add) on independent data: "
+                                                   "the forward's instruction mix without its memory traffic "
+                                                   "or dependency stalls; context, not the peak"}},
         "decode": {"value": round(gbs, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -405,12 +416,13 @@ def read_ceiling(alibi, tensors, dev, workgroups=4096, warmup=2, steps=5):
     return nbytes * steps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def mfma_ceiling(alibi, dev, between, workgroups=1024, iters=160, warmup=5, steps=20):
+def mfma_ceiling(alibi, dev, between, valu=0, workgroups=1024, iters=160, warmup=5, steps=20):
     """TFLOP/s of back-to-back register-fed bf16 MFMAs on every SIMD (two waves
     per SIMD, random N(0, 1) operands like the forward's): the matrix rate the
-    part sustains, beside the forward's rate. Timed the way the benchmark step
-    runs the forward: launches of ~0.5 ms, each followed by `between` (the
-    decode), only the MFMA launches inside the events."""
+    part sustains, beside the forward's rate; with valu=1 each MFMA is joined by
+    the forward's per-MFMA softmax vector work on independent data. Timed the
+    way the benchmark step runs the forward: launches of ~0.5 ms, each followed
+    by `between` (the decode), only the MFMA launches inside the events."""
     import torch
     lib = alibi.load_library()
     g = torch.Generator(device=dev)
@@ -420,7 +432,7 @@ def mfma_ceiling(alibi, dev, between, workgroups=1024, iters=160, warmup=5, step
     st = torch.cuda.current_stream().cuda_stream
 
     def once():
-        rc = lib.alibi_debug_mfma_rate(frags.data_ptr(), iters, sink.data_ptr(), workgroups, st)
+        rc = lib.alibi_debug_mfma_rate(frags.data_ptr(), iters, valu, sink.data_ptr(), workgroups, st)
         assert rc == 0, rc
 
     for _ in range(warmup):
@@ -598,7 +610,7 @@ def run_only(args, alibi, W, fw, dw, dev):
                             dtype=torch.float32).to(torch.bfloat16)
         sink = torch.empty(8 * wgs, dtype=torch.float32, device=dev)
         st = torch.cuda.current_stream().cuda_stream
-        fn = lambda: lib.alibi_debug_mfma_rate(frags.data_ptr(), iters, sink.data_ptr(), wgs, st)
+        fn = lambda: lib.alibi_debug_mfma_rate(frags.data_ptr(), iters, 0, sink.data_ptr(), wgs, st)
         work, unit = float(wgs) * 8 * iters * 16 * 32768.0, "flop"
     else:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB

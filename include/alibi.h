@@ -380,13 +380,17 @@ int alibi_debug_stream_read(const void* buf, long long bytes, unsigned* sink, in
  * 16-byte aligned) holds the operand fragments as 8 x 64 lanes x 8 bf16: A_0 ..
  * A_3 then B_0 .. B_3, lane l of A holding row l % 32, k = 8 (l / 32) .. + 7,
  * and lane l of B column l % 32 at the same k; chain c accumulates A_c B_m for
- * m = 0 .. 3 in turn. Wave w of workgroup g writes the sum of all its
- * accumulator values, iters * sum_m sum(A_c B_m) summed over c, to
- * sink[8 g + w] (device memory, 4-byte aligned, room for 8 workgroups fp32).
+ * m = 0 .. 3 in turn. valu = 1 adds, beside every MFMA, the vector work the
+ * forward's softmax issues per MFMA (an fma, an exponential, half a bf16
+ * pack, half a bf16 dot, an add) on independent data; valu = 0 runs the
+ * MFMAs alone. Wave w of workgroup g writes the sum of all its accumulator
+ * values, iters * sum_m sum(A_c B_m) summed over c, to sink[8 g + w] (device
+ * memory, 4-byte aligned, room for 8 workgroups fp32) either way.
  * Asynchronous on `stream`. ALIBI_EINVAL for bad arguments (checked before
  * anything is enqueued).
  */
-int alibi_debug_mfma_rate(const void* frags, int iters, float* sink, int workgroups, hipStream_t stream);
+int alibi_debug_mfma_rate(const void* frags, int iters, int valu, float* sink, int workgroups,
+                          hipStream_t stream);
 
 /* Static, never-NULL description of a status code. */
 const char* alibi_status_string(int status);

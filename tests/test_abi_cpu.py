@@ -293,14 +293,16 @@ def test_mfma_rate_validation(lib):
     P = ctypes.c_void_p
     f = lib.alibi_debug_mfma_rate
     ok_frags, ok_sink = P(4096), P(8192)
-    assert f(None, 1, ok_sink, 1, None) == -1
-    assert f(ok_frags, 1, None, 1, None) == -1
-    assert f(P(4100), 1, ok_sink, 1, None) == -1       # fragments not 16-byte aligned
-    assert f(ok_frags, 1, P(8194), 1, None) == -1      # sink not 4-byte aligned
-    assert f(ok_frags, 0, ok_sink, 1, None) == -1
-    assert f(ok_frags, (1 << 20) + 1, ok_sink, 1, None) == -1
-    assert f(ok_frags, 1, ok_sink, 0, None) == -1
-    assert f(ok_frags, 1, ok_sink, 65537, None) == -1
+    assert f(None, 1, 0, ok_sink, 1, None) == -1
+    assert f(ok_frags, 1, 0, None, 1, None) == -1
+    assert f(P(4100), 1, 0, ok_sink, 1, None) == -1       # fragments not 16-byte aligned
+    assert f(ok_frags, 1, 0, P(8194), 1, None) == -1      # sink not 4-byte aligned
+    assert f(ok_frags, 0, 0, ok_sink, 1, None) == -1
+    assert f(ok_frags, (1 << 20) + 1, 0, ok_sink, 1, None) == -1
+    assert f(ok_frags, 1, 2, ok_sink, 1, None) == -1       # valu is 0 or 1
+    assert f(ok_frags, 1, -1, ok_sink, 1, None) == -1
+    assert f(ok_frags, 1, 0, ok_sink, 0, None) == -1
+    assert f(ok_frags, 1, 0, ok_sink, 65537, None) == -1
 
 
 def test_stream_read_validation(lib):
