@@ -41,13 +41,14 @@ bounded sample (whole heads of the same forward, whole (b, h) pairs of the
 same decode), scaled to the same units.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --only fwd|decode|copy|bwd|mfma [--steps K] [--warmup W]
+    python bench.py --only fwd|decode|copy|bwd|mfma|mfma_valu [--steps K] [--warmup W]
     python bench.py --only underflow     (CPU only: the bf16 underflow diagnostic
                                           of the 16384-token workload, fp64 oracle)
 
 `--only` runs a single kernel (`bwd`: the three backward kernels; `copy`: a
 plain device-to-device copy of
-a 1 GiB bf16 tensor; `mfma`: the register-fed MFMA-rate kernel) so that
+a 1 GiB bf16 tensor; `mfma`, `mfma_valu`: the register-fed MFMA-rate kernel,
+alone or with the forward's per-MFMA vector mix) so that
 hardware-counter runs see one kernel; it prints a
 short JSON line and no CPU baseline. The copy calibrates the HBM byte counters.
 """
@@ -150,7 +151,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fwd", "fwd16k", "c1", "c2", "c3", "decode", "copy", "bwd", "mfma",
-                                       "oracle", "underflow"], default=None)
+                                       "mfma_valu", "oracle", "underflow"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -603,14 +604,15 @@ def run_only(args, alibi, W, fw, dw, dev):
                            dtype=torch.float32).to(torch.bfloat16)
         fn = lambda: alibi.attn_bwd(q, k, v, out, dout, lse, s, True)
         work, unit = 2.5 * fwd_flops(fw.B, fw.H, fw.N, fw.d), "flop"
-    elif args.only == "mfma":
+    elif args.only in ("mfma", "mfma_valu"):
         lib = alibi.load_library()
+        valu = int(args.only == "mfma_valu")
         wgs, iters = 1024, 160
         frags = torch.randn(8 * 64 * 8, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
                             dtype=torch.float32).to(torch.bfloat16)
         sink = torch.empty(8 * wgs, dtype=torch.float32, device=dev)
         st = torch.cuda.current_stream().cuda_stream
-        fn = lambda: lib.alibi_debug_mfma_rate(frags.data_ptr(), iters, 0, sink.data_ptr(), wgs, st)
+        fn = lambda: lib.alibi_debug_mfma_rate(frags.data_ptr(), iters, valu, sink.data_ptr(), wgs, st)
         work, unit = float(wgs) * 8 * iters * 16 * 32768.0, "flop"
     else:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
