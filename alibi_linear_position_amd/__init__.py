@@ -47,6 +47,7 @@ EXPORTS = {
     "alibi_debug_schedule": [_I, _I, _I, _P],
     "alibi_debug_fwd_waves": [_I],
     "alibi_debug_fwd_split": [_I],
+    "alibi_debug_bwd_query_blocks": [_I],
     "alibi_debug_fwd_form": [_I, _I, _I, _I, _I, _I, _I, _I, _P],
     "alibi_debug_stream_read": [_P, ctypes.c_longlong, _P, _I, _P],
     "alibi_debug_mfma_rate": [_P, _I, _I, _P, _I, _P],

@@ -394,6 +394,12 @@ int alibi_debug_fwd_form(int B, int H, int Nq, int Nk, int d, int causal, int fl
   return ALIBI_OK;
 }
 
+int alibi_debug_bwd_query_blocks(int qb) {
+  if (qb < 0 || qb > 2) return ALIBI_EINVAL;
+  alibi::set_bwd_query_blocks(qb);
+  return ALIBI_OK;
+}
+
 int alibi_debug_fwd_split(int mode) {
   if (mode < 0 || mode > 2) return ALIBI_EINVAL;
   alibi::set_fwd_split(mode);

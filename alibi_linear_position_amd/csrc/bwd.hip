@@ -36,7 +36,9 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <type_traits>
 
 namespace alibi {
@@ -172,19 +174,27 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 // accumulator set and one set of key rows, so two waves fit on every SIMD, and
 // the two roles' MFMA and VALU work overlap within a step instead of waiting
 // for each other.
-template <int D, bool CAUSAL, int VAR>
+//
+// A query tile is QB blocks of 32 rows. With QB = 2 a step does twice the
+// work per barrier and per staging round, and P goes to the dK waves as fp16
+// (P <= 1; relative error 2^-11, against 2^-8 for bf16, whose hand-off
+// misses the gradient bar) so that the 64-row stages and the P buffers fit in
+// LDS together; with QB = 1 the hand-off is the fp32 P.
+template <int D, bool CAUSAL, int VAR, int QB = 1, bool PH = (QB == 2)>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int H, int N, int nkb, int total,
     const float* __restrict__ slopes, float c1, float scale, float clamp2) {
-  constexpr int NT = 512, BK = 128, BQ = 32;
+  static_assert(QB == 1 || QB == 2, "one or two 32-row query blocks per tile");
+  constexpr int NT = 512, BK = 128, BQ = 32 * QB;
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
   using Tile = SwzTile<D>;             // Q / dO tiles: swizzled rows of 2 D bytes
   constexpr int RBYTES = BQ * Tile::ROWB;
   constexpr int STAGE = 2 * RBYTES + 2 * BQ * 4;
   constexpr int CHUNKS = BQ * CPR;    // 16-byte chunks of Q (and of dO) per tile
-  static_assert(CHUNKS <= NT, "one chunk per thread at most");
+  constexpr int NCH = (CHUNKS + NT - 1) / NT;  // per thread
+  static_assert(CHUNKS <= NT || CHUNKS % NT == 0, "chunks split evenly over the threads");
   __shared__ __attribute__((aligned(16))) unsigned char smem[3 * STAGE];
 
   const int tid = threadIdx.x;
@@ -204,8 +214,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int kw0 = k0 + (wave & 3) * 32;
   const int j = kw0 + l32;  // this lane's key
 
-  // S rows are queries 8 (r / 4) + 4 hi + r % 4 of the tile; seeding register r
-  // with -c2 / c1 (8 (r / 4) + r % 4) leaves one fma for the bias.
+  // S rows are queries 8 (r / 4) + 4 hi + r % 4 of a 32-row block; seeding
+  // register r with -c2 / c1 (8 (r / 4) + r % 4) leaves one fma for the bias.
   f32x16 cinit;
 #pragma unroll
   for (int r = 0; r < 16; ++r) cinit[r] = VAR == 0 ? -c21 * float(8 * (r >> 2) + (r & 3)) : 0.0f;
@@ -215,19 +225,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? k0 / BQ : 0;
 
-  // staging registers of one query tile (one chunk of Q and of dO per thread)
-  u32x4 rq = {0u, 0u, 0u, 0u}, rdo = {0u, 0u, 0u, 0u};
+  // staging registers of one query tile (NCH chunks of Q and of dO per thread)
+  u32x4 rq[NCH], rdo[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) rq[c] = rdo[c] = u32x4{0u, 0u, 0u, 0u};
   float rl = 0.0f, rd = 0.0f;
-  // chunk tid of a tile: global row q0 + tid / CPR, chunk tid % CPR, i.e. byte
-  // 16 tid past the tile's first row; rows past N read as zero
+  // chunk id = tid + NT c of a tile: global row q0 + id / CPR, chunk id % CPR,
+  // i.e. byte 16 id past the tile's first row; rows past N read as zero
   const __amdgpu_buffer_rsrc_t rsq = rows_rsrc<D>(q + base, N), rsdo = rows_rsrc<D>(dout + base, N);
-  const int sto = Tile::off(tid / CPR, tid % CPR);
   auto load_tile = [&](int qt) {
     const int q0 = qt * BQ;
-    if (tid < CHUNKS) {
-      const uint32_t vo = uint32_t(q0) * (D * 2) + uint32_t(tid) * 16u;
-      rq = bload16(rsq, vo);
-      rdo = bload16(rsdo, vo);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int id = tid + NT * c;
+      if (id < CHUNKS) {
+        const uint32_t vo = uint32_t(q0) * (D * 2) + uint32_t(id) * 16u;
+        rq[c] = bload16(rsq, vo);
+        rdo[c] = bload16(rsdo, vo);
+      }
     }
     if (tid < BQ) {
       const bool ok = q0 + tid < N;
@@ -236,9 +251,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
   };
   auto store_tile = [&](unsigned char* st) {
-    if (tid < CHUNKS) {
-      *reinterpret_cast<u32x4*>(st + sto) = rq;
-      *reinterpret_cast<u32x4*>(st + RBYTES + sto) = rdo;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int id = tid + NT * c;
+      if (id < CHUNKS) {
+        const int o = Tile::off(id / CPR, id % CPR);
+        *reinterpret_cast<u32x4*>(st + o) = rq[c];
+        *reinterpret_cast<u32x4*>(st + RBYTES + o) = rdo[c];
+      }
     }
     if (tid < BQ) {
       float* sL = reinterpret_cast<float*>(st + 2 * RBYTES);
@@ -254,17 +274,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       f[ks] = __builtin_bit_cast(bf16x8, a);
     }
   };
-  // S = Q K^T (rows = queries, lane = key) and P = exp2(t - lse2) of one tile
-  auto scores = [&](const unsigned char* sQ, const bf16x8 (&kf)[KS]) {
-    f32x16 s = cinit;
-    lds_mfma_ring<KS, 4>([&](int ks) { return *reinterpret_cast<const bf16x8*>(sQ + (rb ^ (32 * ks))); },
-                         [&](int ks, const bf16x8& a) { s = mfma32(a, kf[ks], s); });
-    return s;
+  // Q K^T (or dO V^T) of the QB blocks of a tile (rows = queries, lane = key),
+  // each LDS fragment read once per block; block b starts from init
+  auto products = [&](const unsigned char* sX, const bf16x8 (&kf)[KS], const f32x16& init, f32x16 (&out)[QB]) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) out[b] = init;
+    lds_mfma_ring<KS * QB, 4>(
+        [&](int n) {
+          return *reinterpret_cast<const bf16x8*>(sX + (n % QB) * 32 * Tile::ROWB + (rb ^ (32 * (n / QB))));
+        },
+        [&](int n, const bf16x8& a) { out[n % QB] = mfma32(a, kf[n / QB], out[n % QB]); });
   };
+  // P = exp2(t - lse2) of block b of a tile whose first row is q0
   auto probs = [&](f32x16& s, const float* sL, int q0, auto open_tag) {
     constexpr bool OPEN = decltype(open_tag)::value;  // no query of the tile precedes a key of the block
     const float bj = c2 * float(j - q0 - 4 * hi);  // t = s c1 + bj on the causal side
-    const bool full = OPEN || (CAUSAL && q0 >= kw0 + 31);  // every query of the tile sees every key of the wave
+    const bool full = OPEN || (CAUSAL && q0 >= kw0 + 31);  // every query of the block sees every key of the wave
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 L = *reinterpret_cast<const f32x4*>(sL + 8 * g + 4 * hi);
@@ -286,9 +311,58 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   };
 
   // P of a tile, computed by the dV wave of each key group and read by the dK
-  // wave of the same group one step later: per group and buffer 16 fp32 values
-  // per lane, quad c of lane l at 16 (64 c + l).
-  __shared__ __attribute__((aligned(16))) float sP[2][4][4][64][4];
+  // wave of the same group one step later: per buffer, group and 32-row block
+  // 16 values per lane, in 16-byte pieces (four fp32 or eight fp16 values),
+  // piece c of lane l at 16 (64 c + l).
+  constexpr int PBYTES = PH ? 32 : 64;  // per lane and block
+  __shared__ __attribute__((aligned(16))) unsigned char sP[2 * 4 * QB * 64 * PBYTES];
+  auto p_slot = [&](int tile, int b) {
+    return reinterpret_cast<u32x4*>(sP + ((((tile - qt0) & 1) * 4 + (wave & 3)) * QB + b) * 64 * PBYTES);
+  };
+  auto put_p = [&](u32x4* dst, const f32x16& p) {
+    if constexpr (PH) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 f = {p[8 * c + 2 * e], p[8 * c + 2 * e + 1]};
+          w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+        }
+        dst[64 * c + lane] = w;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        dst[64 * c + lane] = __builtin_bit_cast(u32x4, f32x4{p[4 * c], p[4 * c + 1], p[4 * c + 2], p[4 * c + 3]});
+    }
+  };
+  auto get_p = [&](const u32x4* src) {
+    f32x16 p;
+    if constexpr (PH) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 w = src[64 * c + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // the word goes through a scalar first: a bit cast taken straight
+          // from the vector element compiled to element 0 for every e
+          const uint32_t x = w[e];
+          const f32x2 f = __builtin_convertvector(__builtin_bit_cast(f16x2, x), f32x2);
+          p[8 * c + 2 * e] = f[0];
+          p[8 * c + 2 * e + 1] = f[1];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 x = __builtin_bit_cast(f32x4, src[64 * c + lane]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[4 * c + e] = x[e];
+      }
+    }
+    return p;
+  };
   // Step t: the dV waves take query tile t (S, P, dV), the dK waves tile t - 1
   // (dP, dS = P (dP - D), dK) with the P the dV waves wrote in step t - 1.
   // Tile t sits in stage t % 3; during step t the stage of tile t - 2 (free
@@ -312,6 +386,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       if (t + 2 < nqt) load_tile(t + 2);
     }
   };
+  // dV^T += dO^T P (or dK^T += Q^T dS): the A operand read transposed from the
+  // tile sT, the B operand the packed accumulator rows of block n16 / 2
+  auto accumulate = [&](const unsigned char* sT, const f32x16 (&x)[QB]) {
+    bf16x8 xb[2 * QB];
+#pragma unroll
+    for (int n16 = 0; n16 < 2 * QB; ++n16) xb[n16] = __builtin_bit_cast(bf16x8, pack8(x[n16 >> 1], 8 * (n16 & 1)));
+    lds_mfma_ring<2 * QB * DB, 4>(
+        [&](int n) { return read_tr<D>(sT, tb0, tb1, 16 * (n % (2 * QB)), 32 * (n / (2 * QB))); },
+        [&](int n, const bf16x8& a) {
+          const int db = n / (2 * QB);
+          acc[db] = mfma32(a, xb[n % (2 * QB)], acc[db]);
+        });
+  };
   if (role == 0) {
     bf16x8 kf[KS];
     load_frags(k, kf);
@@ -322,15 +409,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const unsigned char* st = stage_of(t);
       const int q0 = t * BQ;
       if (OPEN || !CAUSAL || q0 + BQ - 1 >= kw0) {
-        f32x16 p = scores(st, kf);
-        probs(p, reinterpret_cast<const float*>(st + 2 * RBYTES), q0, open_tag);
-        float4* const wp = reinterpret_cast<float4*>(&sP[(t - qt0) & 1][wave & 3][0][0][0]);
+        f32x16 p[QB];
+        products(st, kf, cinit, p);
+        const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) wp[64 * c + lane] = float4{p[4 * c], p[4 * c + 1], p[4 * c + 2], p[4 * c + 3]};
-        const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, pack8(p, 0)), __builtin_bit_cast(bf16x8, pack8(p, 8))};
-        lds_mfma_ring<2 * DB, 4>(
-            [&](int n) { return read_tr<D>(st + RBYTES, tb0, tb1, 16 * (n & 1), 32 * (n >> 1)); },
-            [&](int n, const bf16x8& a) { acc[n >> 1] = mfma32(a, pb[n & 1], acc[n >> 1]); });
+        for (int b = 0; b < QB; ++b) {
+          probs(p[b], sL + 32 * b, q0 + 32 * b, open_tag);
+          put_p(p_slot(t, b), p[b]);
+        }
+        accumulate(st + RBYTES, p);
       }
       stage_next(t);
     };
@@ -354,30 +441,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
       const int q0 = u * BQ;
       if (!CAUSAL || q0 + BQ - 1 >= kw0) {
-        f32x16 dp = f32x16{};
-        lds_mfma_ring<KS, 4>(
-            [&](int ks) { return *reinterpret_cast<const bf16x8*>(st + RBYTES + (rb ^ (32 * ks))); },
-            [&](int ks, const bf16x8& a) { dp = mfma32(a, vf[ks], dp); });
-        const float4* const rp = reinterpret_cast<const float4*>(&sP[(u - qt0) & 1][wave & 3][0][0][0]);
-        f32x16 p;
+        f32x16 dp[QB];
+        products(st + RBYTES, vf, f32x16{}, dp);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float4 x = rp[64 * c + lane];
-          p[4 * c] = x.x;
-          p[4 * c + 1] = x.y;
-          p[4 * c + 2] = x.z;
-          p[4 * c + 3] = x.w;
+        for (int b = 0; b < QB; ++b) {
+          const f32x16 p = get_p(p_slot(u, b));
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 Dv = *reinterpret_cast<const f32x4*>(sL + BQ + 32 * b + 8 * g + 4 * hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[b][4 * g + e] = p[4 * g + e] * (dp[b][4 * g + e] - Dv[e]);  // dS
+          }
         }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 Dv = *reinterpret_cast<const f32x4*>(sL + BQ + 8 * g + 4 * hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[4 * g + e] *= dp[4 * g + e] - Dv[e];  // dS = P (dP - D)
-        }
-        const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, pack8(p, 0)), __builtin_bit_cast(bf16x8, pack8(p, 8))};
-        lds_mfma_ring<2 * DB, 4>(
-            [&](int n) { return read_tr<D>(st, tb0, tb1, 16 * (n & 1), 32 * (n >> 1)); },
-            [&](int n, const bf16x8& a) { acc[n >> 1] = mfma32(a, sb[n & 1], acc[n >> 1]); });
+        accumulate(st, dp);
       }
       stage_next(t);
     }
@@ -575,6 +651,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   }
 }
 
+// Query blocks of 32 rows per dK/dV step: 1 or 2 (ALIBI_BWD_QB at load time,
+// or set_bwd_query_blocks; 0 = automatic, which takes 2).
+std::atomic<int>& bwd_qb_override() {
+  static std::atomic<int> w{[] {
+    const char* e = std::getenv("ALIBI_BWD_QB");
+    const int n = e != nullptr ? std::atoi(e) : 0;
+    return (n == 1 || n == 2) ? n : 0;
+  }()};
+  return w;
+}
+// 64-row query tiles measure faster in every form (B8 H16 N4096 d128: 2.01 vs
+// 2.14 ms for the whole backward; B4 H12 N2048 d64: 0.154 vs 0.169 ms).
+int bwd_query_blocks() {
+  const int o = bwd_qb_override().load(std::memory_order_relaxed);
+  return o != 0 ? o : 2;
+}
+
 template <int D, bool CAUSAL, int VAR>
 hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, hipStream_t stream) {
   const long long rows = (long long)a.B * a.H * a.N;
@@ -586,10 +679,16 @@ hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, 
   const float scale = float(1.0 / std::sqrt(double(D)));
   const int nkb = (a.N + 127) / 128;
   const long long tk = (long long)a.B * a.H * nkb;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VAR>), dim3(unsigned(tk)), dim3(512), 0, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
-                     nkb, int(tk), a.slopes, c1, scale, a.clamp2);
+  if (bwd_query_blocks() == 2)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VAR, 2>), dim3(unsigned(tk)), dim3(512), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
+                       nkb, int(tk), a.slopes, c1, scale, a.clamp2);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VAR, 1>), dim3(unsigned(tk)), dim3(512), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
+                       nkb, int(tk), a.slopes, c1, scale, a.clamp2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.N + 127) / 128;
@@ -616,6 +715,8 @@ hipError_t launch_bwd_var(const BwdArgs& a, float* dsum, float* lse2, float c1, 
 }
 
 }  // namespace
+
+void set_bwd_query_blocks(int qb) { bwd_qb_override().store(qb, std::memory_order_relaxed); }
 
 hipError_t launch_bwd(const BwdArgs& a, float* ws, float c1, hipStream_t stream) {
   float* dsum = ws;

@@ -61,6 +61,8 @@ struct BwdArgs {
 
 // Backward, d in {64, 128}; ws holds 2 B H N floats (D and lse in log2 units).
 hipError_t launch_bwd(const BwdArgs& a, float* ws, float c1, hipStream_t stream);
+// 32-row query blocks per dK/dV step: 0 = automatic (the default: 2), 1 or 2.
+void set_bwd_query_blocks(int qb);
 
 // Generic (VALU) forward, any d <= 256: fp32 (f32 = true) or bf16 data.
 hipError_t launch_fwd_generic(const FwdArgs& a, const FwdOptions& opt, bool f32, hipStream_t stream);

@@ -348,6 +348,17 @@ int alibi_debug_fwd_waves(int nw);
 int alibi_debug_fwd_split(int mode);
 
 /*
+ * TEST AND TUNING ONLY: 32-row query blocks per step of the backward's dK/dV
+ * kernel, process-wide. 0 = automatic (the default, which takes 2), 1 or 2 =
+ * forced for every later call. With 2, each step takes a 64-row query tile and the weights P
+ * pass from the dV to the dK waves as fp16 (fp32 with 1); the gradients
+ * differ by rounding only. The environment variable ALIBI_BWD_QB=1|2, read
+ * once at load, sets the same override. Not synchronised with launches in
+ * flight on other threads. ALIBI_EINVAL for other values.
+ */
+int alibi_debug_bwd_query_blocks(int qb);
+
+/*
  * TEST AND TUNING ONLY: the form a bf16 forward call with these sizes would
  * launch, under the current overrides. flags: the ALIBI_* option bits; delta:
  * q_offset - k_offset. *form: 0 = the generic kernel (d not 64 or 128), 4 or 8

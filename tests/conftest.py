@@ -54,3 +54,14 @@ def fwd_waves(request):
     assert lib.alibi_debug_fwd_waves(request.param) == 0
     yield request.param
     assert lib.alibi_debug_fwd_waves(0) == 0
+
+
+@pytest.fixture(params=[1, 2], ids=["qb1", "qb2"])
+def bwd_form(request):
+    """Forces the backward's dK/dV kernel to 32-row (fp32 P hand-off) or 64-row
+    (fp16 P hand-off) query tiles for one test."""
+    import alibi_linear_position_amd as alibi
+    lib = alibi.load_library()
+    assert lib.alibi_debug_bwd_query_blocks(request.param) == 0
+    yield request.param
+    assert lib.alibi_debug_bwd_query_blocks(0) == 0

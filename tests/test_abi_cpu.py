@@ -288,6 +288,14 @@ def test_fwd_split_override_validation(lib):
     assert lib.alibi_debug_fwd_split(0) == 0
 
 
+def test_bwd_query_blocks_switch(lib):
+    for qb in (0, 1, 2):
+        assert lib.alibi_debug_bwd_query_blocks(qb) == 0
+    for qb in (-1, 3, 4):
+        assert lib.alibi_debug_bwd_query_blocks(qb) == -1
+    assert lib.alibi_debug_bwd_query_blocks(0) == 0
+
+
 def test_mfma_rate_validation(lib):
     # host-side checks only: every bad argument is refused before any launch
     P = ctypes.c_void_p

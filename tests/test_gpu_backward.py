@@ -76,14 +76,14 @@ def _inputs(shape, seed):
     # shorter than one tile, a single token, and a non-causal multi-tile d = 128 case
     (1, 2, 129, 128, True), (1, 3, 16, 64, True), (1, 2, 1, 128, True), (2, 2, 160, 128, False),
 ])
-def test_backward_small(alibi, B, H, N, d, causal):
+def test_backward_small(alibi, bwd_form, B, H, N, d, causal):
     q, k, v, do = _inputs((B, H, N, d), 31)
     s = oracle.slopes_ref(H)
     qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
     out, lse = alibi.attn_fwd_train(qd, kd, vd, torch.from_numpy(s), causal)
     dq, dk, dv = alibi.attn_bwd(qd, kd, vd, out, dod, lse, torch.from_numpy(s), causal)
     torch.cuda.synchronize()
-    tag = f"B{B} H{H} N{N} d{d} causal={causal}"
+    tag = f"B{B} H{H} N{N} d{d} causal={causal} qb={bwd_form}"
     dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
     for b in range(B):
         for h in range(H):
@@ -203,7 +203,7 @@ def _mit_ids(x):
     (1, 2, 300, 128, True), (1, 3, 129, 64, True), (2, 2, 200, 64, False), (1, 2, 513, 128, False),
     (1, 2, 33, 128, True),
 ])
-def test_backward_mitigations(alibi, mit, B, H, N, d, causal):
+def test_backward_mitigations(alibi, bwd_form, mit, B, H, N, d, causal):
     clamp, logd = mit
     q, k, v, do = _inputs((B, H, N, d), 61)
     s = oracle.slopes_recipe_ref("steep", H, logd)
@@ -214,7 +214,7 @@ def test_backward_mitigations(alibi, mit, B, H, N, d, causal):
                                 log_distance=logd)
     torch.cuda.synchronize()
     dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
-    tag = f"{_mit_ids(mit)} B{B} H{H} N{N} d{d} causal={causal}"
+    tag = f"{_mit_ids(mit)} B{B} H{H} N{N} d{d} causal={causal} qb={bwd_form}"
     for b in range(B):
         for h in range(H):
             check_grads((dq[b, h], dk[b, h], dv[b, h]), q[b, h], k[b, h], v[b, h], do[b, h], float(s[h]), causal,
