@@ -14,13 +14,14 @@
 //   per row.
 // * bwd_dkdv_kernel: one workgroup per 128 keys of one (b, h), eight waves:
 //   four own dV and four own dK of 32 keys each, keeping their keys' K (or V)
-//   rows as MFMA B operands in registers. Query tiles of 32 rows stream
-//   through a three-stage LDS ring: read straight for S = Q K^T and
+//   rows as MFMA B operands in registers. Query tiles of 64 rows (or 32)
+//   stream through a three-stage LDS ring: read straight for S = Q K^T and
 //   dP = dO V^T (rows = queries, lane = key), and read transposed
 //   (ds_read_b64_tr_b16) for dV^T += dO^T P and dK^T += Q^T dS, so P and dS go
 //   from registers to the next MFMA as B operands. The dV waves compute P once
-//   and hand it to the dK waves through LDS; the dK waves run one query tile
-//   behind, so both roles work at the same time between barriers.
+//   and hand it to the dK waves through LDS (fp16 with 64-row tiles, fp32 with
+//   32-row ones); the dK waves run one query tile behind, so both roles work
+//   at the same time between barriers.
 // * bwd_dq_kernel: one workgroup per 128 queries, the forward's layout:
 //   S^T = K Q^T and dP^T = V dO^T (lane = query, so lse and D are one value
 //   per lane), dS^T packed to bf16 and dQ^T += K^T dS^T, with K^T read

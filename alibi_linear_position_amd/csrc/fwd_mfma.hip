@@ -13,14 +13,18 @@
 // ------------------
 // * A workgroup is NW = 4 or 8 waves and owns BM = 32 NW consecutive query
 //   rows of one (b, h); each wave owns 32 rows. Two waves share each SIMD (at
-//   most 256 registers per lane; two 4-wave or one 8-wave workgroup per CU), so
-//   one wave's MFMA work can overlap the other's softmax arithmetic.
+//   most 256 registers per lane; two 4-wave or one 8-wave workgroup per CU);
+//   the barrier of every tile keeps the two in phase, so the time of a tile is
+//   close to its MFMA time plus its softmax time.
 // * Key/value tiles of BN = 64 rows are staged HBM -> registers -> LDS by the
-//   whole workgroup: K row-major (16-byte coalesced loads, rows padded by 16 B
-//   against bank conflicts), V transposed to V^T[d][key] (one key per lane,
-//   16-bit LDS writes) so every wave reads its MFMA A operand with 16-byte LDS
-//   reads. LDS is double-buffered: the loads of the next tile are in flight
-//   while the current one is computed, with one barrier per tile.
+//   whole workgroup through buffer resources: K row-major (16-byte coalesced
+//   loads, rows padded by 16 B against bank conflicts), V transposed to
+//   V^T[d][key], each thread loading the same 8 d of 2 or 4 consecutive keys
+//   and writing them per d as one 4- or 8-byte store (v_perm_b32), so every
+//   wave reads its MFMA A operands with 16-byte LDS reads, four fragments
+//   ahead of their MFMAs. LDS is double-buffered: the loads of the next tile
+//   are in flight while the current one is computed, with one barrier per
+//   tile.
 // * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (M = 32 keys, N = 32 queries,
 //   K = 16 of d). In the 32x32 accumulator layout lane l holds one query
 //   (l % 32) and 16 of the 32 keys, so the row softmax is almost entirely
@@ -36,12 +40,14 @@
 //   true one, older tiles carry a smaller bias, and the accumulator is rescaled
 //   only when the maximum grows by more than 2^8 (lazy rescale; exact up to
 //   fp32 rounding because numerator and denominator share the scale).
-//   Off-diagonal tiles use a cheap upper bound of the row maximum
-//   (max_j s_ij * c1 plus the largest bias in the tile) instead of the exact
-//   maximum; any bound works for the algebra and this one keeps p <= 2^8.
+//   Tiles under the causal mask form the row maximum from the tile; tiles with
+//   every key visible exponentiate against the running maximum directly and
+//   form a bound of the row maximum (max_j s_ij * c1 plus the largest bias in
+//   the tile) only when a lane's partial row sum leaves (0, 2^16], redoing the
+//   tile then; any bound works for the algebra.
 //   The first Q K^T k-step takes a constant register set as its C operand,
-//   which seeds each score with its register's bias offset, so there the bias
-//   costs one fma per score. Row reductions across the two lane halves use
+//   which seeds each score with its register's bias offset, so the bias costs
+//   one fma per score. Row reductions across the two lane halves use
 //   v_permlane32_swap; row sums use four independent accumulators.
 // * The row sum is accumulated from the bf16-rounded p that the PV product
 //   uses (v_dot2c_f32_bf16), so the normalisation matches the numerator.
