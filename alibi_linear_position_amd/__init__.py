@@ -59,6 +59,8 @@ EXPORTS = {
     "alibi_attn_decode_ws": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_size_t, _P],
     "alibi_debug_fail_allocations": [_I],
     "alibi_attn_decode_noalloc": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P],
+    "alibi_attn_decode_ex": [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P],
+    "alibi_key_norm_max": [_P, _I, _I, _I, _I, _P, _P],
 }
 _RESTYPES = {"alibi_status_string": ctypes.c_char_p, "alibi_decode_ws_bytes": ctypes.c_size_t}
 
@@ -72,6 +74,11 @@ class FwdOpts(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_int), ("clamp_min", ctypes.c_float), ("softcap", ctypes.c_float),
                 ("q_offset", ctypes.c_int), ("k_offset", ctypes.c_int), ("lse", ctypes.c_void_p),
                 ("window", ctypes.c_void_p)]
+
+
+class DecodeOpts(ctypes.Structure):
+    """Mirror of struct alibi_decode_opts."""
+    _fields_ = [("flags", ctypes.c_int), ("key_norm_max", ctypes.c_void_p)]
 
 
 _lib = None
@@ -303,6 +310,56 @@ def attn_decode(q, kcache, vcache, slopes=None, out=None):
             _P(q.data_ptr()), _P(kcache.data_ptr()), _P(vcache.data_ptr()), _P(out.data_ptr()),
             B, H, L, d, _P(s.data_ptr()), _stream_handle(q.device))
     _check("alibi_attn_decode", st)
+    return out
+
+
+def key_norm_max(kcache):
+    """max_j |k_j| per (b, h) of a bf16 cache (B, H, L, d), d in {64, 128}:
+    fp32 (B, H) on the cache's device (the bound attn_decode_ex skips with)."""
+    import torch
+    _need(kcache, torch.bfloat16, 4, "kcache")
+    B, H, L, d = kcache.shape
+    out = torch.empty((B, H), dtype=torch.float32, device=kcache.device)
+    with torch.cuda.device(kcache.device):
+        st = load_library().alibi_key_norm_max(_P(kcache.data_ptr()), B, H, L, d, _P(out.data_ptr()),
+                                               _stream_handle(kcache.device))
+    _check("alibi_key_norm_max", st)
+    return out
+
+
+def attn_decode_ex(q, kcache, vcache, slopes=None, skip_underflow=False, key_norm_max=None, out=None):
+    """attn_decode with options: skip_underflow=True skips, exactly, the cached
+    keys whose weights round to zero, given key_norm_max (fp32 (B, H) on the
+    device: an upper bound of every key norm of each (b, h), e.g. from
+    key_norm_max(kcache))."""
+    import torch
+    _need(q, torch.bfloat16, 3, "q")
+    _need(kcache, torch.bfloat16, 4, "kcache")
+    _need(vcache, torch.bfloat16, 4, "vcache")
+    B, H, L, d = kcache.shape
+    if vcache.shape != kcache.shape or tuple(q.shape) != (B, H, d):
+        raise ValueError("expected q (B, H, d) and caches (B, H, L, d)")
+    s = _slopes_dev(slopes, H, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, torch.bfloat16, 3, "out")
+    opts = DecodeOpts()
+    opts.flags = 0
+    opts.key_norm_max = None
+    if skip_underflow:
+        if key_norm_max is None:
+            raise ValueError("skip_underflow needs key_norm_max")
+        if key_norm_max.dtype != torch.float32 or key_norm_max.device != q.device or \
+                tuple(key_norm_max.shape) != (B, H) or not key_norm_max.is_contiguous():
+            raise ValueError("key_norm_max must be a contiguous fp32 (B, H) tensor on q's device")
+        opts.flags = SKIP_UNDERFLOW
+        opts.key_norm_max = key_norm_max.data_ptr()
+    with torch.cuda.device(q.device):
+        st = load_library().alibi_attn_decode_ex(
+            _P(q.data_ptr()), _P(kcache.data_ptr()), _P(vcache.data_ptr()), _P(out.data_ptr()),
+            B, H, L, d, _P(s.data_ptr()), ctypes.byref(opts), _stream_handle(q.device))
+    _check("alibi_attn_decode_ex", st)
     return out
 
 

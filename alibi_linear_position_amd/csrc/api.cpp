@@ -142,13 +142,14 @@ size_t decode_ws_bytes(int B, int H, int L, int d) {
 }
 
 int launch_decode_plan(const void* q, const void* kcache, const void* vcache, void* out, int B, int H, int L,
-                       int d, const float* slopes, float* ws, hipStream_t stream) {
+                       int d, const float* slopes, float* ws, hipStream_t stream, const float* knorm = nullptr) {
   int splits = 1, chunk = L;
   alibi::decode_plan(B, H, L, d, &splits, &chunk);
   if (log_enabled())
-    std::fprintf(stderr, "[alibi] decode B=%d H=%d L=%d d=%d splits=%d chunk=%d\n", B, H, L, d, splits, chunk);
+    std::fprintf(stderr, "[alibi] decode B=%d H=%d L=%d d=%d splits=%d chunk=%d skip=%d\n", B, H, L, d, splits, chunk,
+                 int(knorm != nullptr));
   return hip_status(alibi::launch_decode(q, kcache, vcache, out, ws, B, H, L, d, splits, chunk, slopes,
-                                         scale_log2(d), stream));
+                                         scale_log2(d), knorm, stream));
 }
 
 }  // namespace
@@ -297,6 +298,49 @@ int alibi_attn_decode(const void* q, const void* kcache, const void* vcache, voi
     if (st != ALIBI_OK) return st;
   }
   return launch_decode_plan(q, kcache, vcache, out, B, H, L, d, slopes, ws, stream);
+}
+
+int alibi_attn_decode_ex(const void* q, const void* kcache, const void* vcache, void* out, int B, int H, int L,
+                         int d, const float* slopes, const alibi_decode_opts* opts, hipStream_t stream) {
+  int st = check_decode(q, kcache, vcache, out, slopes, B, H, L, d);
+  if (st != ALIBI_OK) return st;
+  const float* knorm = nullptr;
+  if (opts != nullptr) {
+    if ((opts->flags & ~ALIBI_SKIP_UNDERFLOW) != 0) return ALIBI_EINVAL;
+    if (opts->flags & ALIBI_SKIP_UNDERFLOW) {
+      if (opts->key_norm_max == nullptr || !aligned(opts->key_norm_max, 4)) return ALIBI_EINVAL;
+      knorm = opts->key_norm_max;
+    }
+  }
+  float* ws = nullptr;
+  const size_t bytes = decode_ws_bytes(B, H, L, d);
+  if (bytes > 0) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    st = workspace_get(kDecode, bytes, &ws);
+    if (st != ALIBI_OK) return st;
+  }
+  return launch_decode_plan(q, kcache, vcache, out, B, H, L, d, slopes, ws, stream, knorm);
+}
+
+int alibi_key_norm_max(const void* kcache, int B, int H, int L, int d, float* out, hipStream_t stream) {
+  if (kcache == nullptr || out == nullptr || B < 1 || H < 1 || L < 1 || d < 1 || L > kMaxLen ||
+      !aligned(kcache, 16) || !aligned(out, 4))
+    return ALIBI_EINVAL;
+  if (d != 64 && d != 128) return ALIBI_ENOTSUP;
+  if ((long long)B * H * L > (1LL << 31) * 4) return ALIBI_ENOTSUP;
+  // partial maxima over key ranges of at least 256 rows, enough of them to
+  // keep the part's loads in flight, then one maximum per (b, h)
+  const long long bh = (long long)B * H;
+  const int parts = int(std::max(1LL, std::min(std::max(1LL, (long long)L / 256), (4096 + bh - 1) / bh)));
+  float* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    const int st = workspace_get(kNorm, (size_t)bh * parts * sizeof(float), &ws);
+    if (st != ALIBI_OK) return st;
+  }
+  const int st = hip_status(alibi::launch_knorm_max(kcache, ws, B, H, L, d, parts, stream));
+  if (st != ALIBI_OK) return st;
+  return hip_status(alibi::launch_knorm_reduce(ws, out, bh, parts, stream));
 }
 
 int alibi_attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, void* out, int B, int H,

@@ -12,6 +12,21 @@
 // grows by more than 2^8 (a lazy rescale, exact up to fp32 rounding).
 // Partial softmax states (m, l, acc) of the key ranges are merged with the
 // stable-softmax algebra of "When Attention Goes Blind", App. B.1-B.2.
+//
+// Exact underflow skipping (knorm != null: an upper bound of |k_j| over the
+// cache of each (b, h)): every score is at most A - c2 D with
+// A = |q| max|k| c1 (Cauchy-Schwarz; D the distance L - 1 - j, scores in log2
+// units), and the score of key L - 1 is at least -A. The combined maximum is
+// therefore at least -A, so a key range whose nearest key lies at D0 with
+// c2 D0 > 2 A + 152 enters the combine with weight 2^(m_s - M) < 2^-150, an
+// exact zero: it is not read at all. Inside a range, a key group's running
+// maximum is at least its first key's score, at most G - 1 keys behind the
+// range's nearest one, so keys beyond D0 + G - 1 + (2 A + 152) / c2 give
+// exp2 values below 2^-150, exact zeros that cannot move the maximum either:
+// the walk, newest keys first, stops there. The output is bit for bit the
+// unskipped one whenever the bound holds (and the caches are finite); most of
+// a steep head's cache is then never read ("When Attention Goes Blind",
+// Sec. 3.3 and 5.1-5.2: the weights of distant keys underflow to zero).
 #include "device_common.h"
 #include "launch.h"
 
@@ -40,7 +55,7 @@ template <int LPK>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     uint16_t* __restrict__ out, float* __restrict__ ws, int H, int L, int d, int splits, int chunk,
-    const float* __restrict__ slopes, float c1) {
+    const float* __restrict__ slopes, float c1, const float* __restrict__ knorm) {
   constexpr int G = kDecodeThreads / LPK;  // key groups per workgroup
   constexpr int U = kDecodeUnroll;
   __shared__ float sm_m[G];
@@ -76,7 +91,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 
   const uint16_t* kbase = kc + bh * (long long)L * d + sub * 8;
   const uint16_t* vbase = vc + bh * (long long)L * d + sub * 8;
-  const int n_iter = (jend - jbeg + G * U - 1) / (G * U);
+  int n_iter = (jend - jbeg + G * U - 1) / (G * U);
+  if (knorm != nullptr && c2 > 0.0f) {
+    // |q| from the bf16 query (qf holds q c1), with the key bound and a
+    // relative margin of 2^-8 against rounding
+    float qn2 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qn2 = fmaf(qf[e], qf[e], qn2);
+    const float A = sqrtf(group_sum<LPK>(qn2)) * knorm[bh] * (1.0f + 1.0f / 256.0f);
+    const float reach = (2.0f * A + 152.0f) / c2;  // keys past a maximum's key that underflow
+    const float d0 = float(L - jend);                // distance of the range's nearest key
+    if (d0 > reach) {
+      n_iter = 0;  // the whole range: weight zero in the combine
+    } else if (reach < float(1 << 30)) {
+      // iteration it starts at distance d0 + it G U: skip it once that is past
+      // d0 + G - 1 + reach
+      const int keep = int((float(G - 1) + reach) / float(G * U)) + 1;
+      n_iter = min(n_iter, keep);
+    }
+  }
   for (int it = 0; it < n_iter; ++it) {
     u32x4 kr[U], vr[U];
     int jj[U];
@@ -183,11 +216,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 template <int LPK>
 hipError_t launch_split(const void* q, const void* kc, const void* vc, void* out, float* ws,
                         int B, int H, int L, int d, int splits, int chunk, const float* slopes,
-                        float c1, hipStream_t stream) {
+                        float c1, const float* knorm, hipStream_t stream) {
   const unsigned grid = unsigned((long long)B * H * splits);
   hipLaunchKernelGGL(decode_split_kernel<LPK>, dim3(grid), dim3(kDecodeThreads), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, (uint16_t*)out,
-                     ws, H, L, d, splits, chunk, slopes, c1);
+                     ws, H, L, d, splits, chunk, slopes, c1, knorm);
   return hipGetLastError();
 }
 
@@ -228,14 +261,14 @@ void decode_plan(int B, int H, int L, int d, int* splits, int* chunk) {
 
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* out, float* ws,
                          int B, int H, int L, int d, int splits, int chunk,
-                         const float* slopes, float c1, hipStream_t stream) {
+                         const float* slopes, float c1, const float* knorm, hipStream_t stream) {
   hipError_t e;
   const int lpk = (d + 7) / 8;
-  if (lpk <= 2) e = launch_split<2>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, stream);
-  else if (lpk <= 4) e = launch_split<4>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, stream);
-  else if (lpk <= 8) e = launch_split<8>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, stream);
-  else if (lpk <= 16) e = launch_split<16>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, stream);
-  else e = launch_split<32>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, stream);
+  if (lpk <= 2) e = launch_split<2>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, knorm, stream);
+  else if (lpk <= 4) e = launch_split<4>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, knorm, stream);
+  else if (lpk <= 8) e = launch_split<8>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, knorm, stream);
+  else if (lpk <= 16) e = launch_split<16>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, knorm, stream);
+  else e = launch_split<32>(q, kc, vc, out, ws, B, H, L, d, splits, chunk, slopes, c1, knorm, stream);
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(unsigned((long long)B * H)), dim3(256), 0, stream,
                      (const float*)ws, (uint16_t*)out, d, splits);

@@ -7,7 +7,8 @@
 // be shown to give exp() values that round to zero, which is the underflow the
 // blindness analysis of "When Attention Goes Blind" (Sec. 3.2-3.3, Sec. 5.1)
 // describes. This pass produces max_j |k_j| for each (b, h) as P partial maxima
-// (the forward takes the max of the P values): workgroup (b h, p) covers rows
+// (the forward takes the max of the P values; for the decode a second kernel
+// reduces them to one bound per (b, h)): workgroup (b h, p) covers rows
 // p N / P .. (p + 1) N / P - 1. The pass reads K once (B H N d bf16).
 #include "device_common.h"
 #include "launch.h"
@@ -52,7 +53,22 @@ __global__ __launch_bounds__(kNormThreads) void knorm_max_kernel(const uint16_t*
   }
 }
 
+// out[i] = max_p part[i P + p], one thread per (b, h).
+__global__ __launch_bounds__(256) void knorm_reduce_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                           long long n, int P) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float m = 0.0f;
+  for (int p = 0; p < P; ++p) m = fmaxf(m, part[i * P + p]);
+  out[i] = m;
+}
+
 }  // namespace
+
+hipError_t launch_knorm_reduce(const float* part, float* out, long long n, int P, hipStream_t stream) {
+  hipLaunchKernelGGL(knorm_reduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, part, out, n, P);
+  return hipGetLastError();
+}
 
 hipError_t launch_knorm_max(const void* k, float* out, int B, int H, int N, int d, int P,
                             hipStream_t stream) {

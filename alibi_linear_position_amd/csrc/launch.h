@@ -90,12 +90,16 @@ hipError_t launch_mfma_rate(const void* frags, int iters, bool valu, float* sink
                             hipStream_t stream);
 hipError_t launch_knorm_max(const void* k, float* out, int B, int H, int N, int d, int P,
                             hipStream_t stream);
+// out[i] = max over p of part[i P + p], i < n.
+hipError_t launch_knorm_reduce(const float* part, float* out, long long n, int P, hipStream_t stream);
 
 // Split-KV decode. `splits` key ranges of `chunk` keys each; ws holds
 // B*H*splits*(d+2) floats when splits > 1 (may be null when splits == 1).
+// knorm: null, or B*H upper bounds of the key norms for exact underflow
+// skipping.
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* out, float* ws,
                          int B, int H, int L, int d, int splits, int chunk,
-                         const float* slopes, float c1, hipStream_t stream);
+                         const float* slopes, float c1, const float* knorm, hipStream_t stream);
 
 // Number of splits and keys per split the decode launcher will use.
 void decode_plan(int B, int H, int L, int d, int* splits, int* chunk);

@@ -147,6 +147,50 @@ int alibi_attn_decode_noalloc(const void* q, const void* kcache, const void* vca
                               int B, int H, int L, int d, const float* slopes, hipStream_t stream);
 
 /*
+ * Options of alibi_attn_decode_ex. flags: 0 or ALIBI_SKIP_UNDERFLOW (defined
+ * below with the forward's options); other bits -> ALIBI_EINVAL.
+ */
+typedef struct alibi_decode_opts {
+  int flags;
+  const float* key_norm_max; /* device, B H fp32 (4-byte aligned): for each (b, h) an upper
+                                bound of |k_j| over the whole key cache, e.g. from
+                                alibi_key_norm_max; required with ALIBI_SKIP_UNDERFLOW */
+} alibi_decode_opts;
+
+/*
+ * The decode with options (opts NULL or flags 0: alibi_attn_decode).
+ * ALIBI_SKIP_UNDERFLOW skips, exactly, the cached keys whose weights round to
+ * zero: every score is at most A - m_h D with A = |q| key_norm_max / sqrt(d)
+ * and D the key's distance, and the newest key's score is at least -A, so a
+ * key more than (2 A + 152 ln 2) / m_h behind the keys that set the running
+ * maxima has exp() below 2^-150 relative to them, an exact zero in fp32 ("When
+ * Attention Goes Blind", Sec. 3.3 and 5.1-5.2: distant weights underflow). Key
+ * ranges past that distance are not read, and the walk inside a range stops
+ * there, so a steep head reads only its last few hundred keys. The output is
+ * bitwise the output of alibi_attn_decode when key_norm_max bounds every key
+ * norm of its (b, h) and the caches are finite; a smaller bound gives a wrong
+ * result, not a fault. A caller that appends keys keeps the bound current as
+ * max(bound, |k_new|). Uses the library's decode workspace (ordering as
+ * alibi_attn_decode). Errors: as alibi_attn_decode, plus ALIBI_EINVAL for an
+ * unknown flag or a missing or misaligned key_norm_max.
+ */
+int alibi_attn_decode_ex(const void* q, const void* kcache, const void* vcache, void* out,
+                         int B, int H, int L, int d, const float* slopes, const alibi_decode_opts* opts,
+                         hipStream_t stream);
+
+/*
+ * The bound alibi_attn_decode_ex's skipping takes: out[b H + h] (device fp32,
+ * 4-byte aligned) = max_j |k_j| over the L keys of (b, h) of a bf16 cache
+ * (B, H, L, d), d in {64, 128} (ALIBI_ENOTSUP otherwise), computed in fp32 from
+ * the bf16 values (the decode adds a relative margin of 2^-8 against
+ * rounding). Reads the cache once; partial maxima go through the library's
+ * key-norm workspace (ordering as the other workspaces, ALIBI_ENOMEM if it
+ * cannot be allocated). Asynchronous on `stream`. ALIBI_EINVAL for NULL or
+ * misaligned pointers or sizes < 1.
+ */
+int alibi_key_norm_max(const void* kcache, int B, int H, int L, int d, float* out, hipStream_t stream);
+
+/*
  * TEST ONLY, not on the hot path: materialises the fp32 attention weights
  * w (B, H, N, N) of the fp32 forward, so the printed weight matrices of the
  * 4-head seed-42 example can be checked on the device. Masked weights are

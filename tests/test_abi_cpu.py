@@ -122,6 +122,32 @@ def test_decode_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 128, None, None) == -1
 
 
+def test_decode_ex_validation(lib):
+    import ctypes
+    import alibi_linear_position_amd as alibi
+    f = lib.alibi_attn_decode_ex
+    bad = alibi.DecodeOpts(flags=1, key_norm_max=None)            # an unknown bit
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 128, FAKE, ctypes.byref(bad), None) == -1
+    missing = alibi.DecodeOpts(flags=alibi.SKIP_UNDERFLOW, key_norm_max=None)
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 128, FAKE, ctypes.byref(missing), None) == -1
+    misaligned = alibi.DecodeOpts(flags=alibi.SKIP_UNDERFLOW, key_norm_max=4098)
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 128, FAKE, ctypes.byref(misaligned), None) == -1
+    # the decode's own checks come first
+    assert f(None, FAKE, FAKE, FAKE, 1, 1, 8, 128, FAKE, None, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 127, FAKE, None, None) == -2
+
+
+def test_key_norm_max_validation(lib):
+    f = lib.alibi_key_norm_max
+    assert f(None, 1, 1, 8, 128, FAKE, None) == -1
+    assert f(FAKE, 1, 1, 8, 128, None, None) == -1
+    assert f(FAKE + 4, 1, 1, 8, 128, FAKE, None) == -1     # cache not 16-byte aligned
+    assert f(FAKE, 1, 1, 8, 128, FAKE + 2, None) == -1     # out not 4-byte aligned
+    assert f(FAKE, 0, 1, 8, 128, FAKE, None) == -1
+    assert f(FAKE, 1, 1, 0, 128, FAKE, None) == -1
+    assert f(FAKE, 1, 1, 8, 96, FAKE, None) == -2          # d other than 64 or 128
+
+
 def test_weights_validation(lib):
     f = lib.alibi_attn_weights_f32
     assert f(FAKE, FAKE, FAKE, 1, 1, 1025, 16, FAKE, 1, None) == -2
