@@ -86,7 +86,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ALIBI_OK : ALIBI_EHIP; }
 
 // ---- library workspaces: growable buffers per device ----
 // kDecode holds the decode's partial softmax states, kNorm the key-norm maxima
-// of the skipping forward, kBwd the backward's row terms. All are used asynchronously on the caller's stream.
+// of the skipping forward, kBwd the backward's row terms (and its norm maxima when it skips). All are used asynchronously on the caller's stream.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -232,6 +232,7 @@ int alibi_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o
   if (causal != 0 && causal != 1) return ALIBI_EINVAL;
   int flags = 0;
   float clamp_min = 0.0f;
+  bool skip = false;
   if (opts != nullptr) {
     if ((opts->flags & ~(ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP | ALIBI_SKIP_UNDERFLOW | ALIBI_WINDOW)) != 0)
       return ALIBI_EINVAL;
@@ -241,19 +242,36 @@ int alibi_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o
       return ALIBI_ENOTSUP;
     flags = opts->flags & (ALIBI_CLAMP | ALIBI_LOG_DISTANCE);
     clamp_min = opts->clamp_min;
+    skip = (opts->flags & ALIBI_SKIP_UNDERFLOW) != 0;
   }
   if (d != 64 && d != 128) return ALIBI_ENOTSUP;
+  // Exact underflow skipping acts on the plain causal form (elsewhere the flag
+  // changes nothing); its bound needs the largest query and key norms per
+  // (b, h), kept as partial maxima behind the row terms in the workspace.
+  skip = skip && causal && flags == 0;
+  const long long bh = (long long)B * H;
+  const int parts = skip ? int(std::max(1LL, std::min(std::max(1LL, (long long)N / 256), (2048 + bh - 1) / bh))) : 0;
   float* ws = nullptr;
   {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    st = workspace_get(kBwd, (size_t)2 * B * H * N * sizeof(float), &ws);
+    st = workspace_get(kBwd, ((size_t)2 * B * H * N + (size_t)2 * bh * parts) * sizeof(float), &ws);
   }
   if (st != ALIBI_OK) return st;
   if (log_enabled())
-    std::fprintf(stderr, "[alibi] bwd B=%d H=%d N=%d d=%d causal=%d flags=%d\n", B, H, N, d, causal, flags);
+    std::fprintf(stderr, "[alibi] bwd B=%d H=%d N=%d d=%d causal=%d flags=%d skip=%d\n", B, H, N, d, causal, flags,
+                 int(skip));
   alibi::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, slopes, causal};
   a.flags = flags;
   a.clamp2 = clamp_min * 1.4426950408889634f;  // as the forward forms its floor (log2 units)
+  if (skip) {
+    float* norms = ws + (size_t)2 * B * H * N;
+    st = hip_status(alibi::launch_knorm_max(k, norms, B, H, N, d, parts, stream));
+    if (st != ALIBI_OK) return st;
+    st = hip_status(alibi::launch_knorm_max(q, norms + bh * parts, B, H, N, d, parts, stream));
+    if (st != ALIBI_OK) return st;
+    a.norms = norms;
+    a.norm_parts = parts;
+  }
   return hip_status(alibi::launch_bwd(a, ws, scale_log2(d), stream));
 }
 

@@ -140,6 +140,32 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int base) {
   return r;
 }
 
+// Exact underflow skipping of the plain causal form. With M_q and M_k the
+// largest query and key norms of a (b, h) pair and A = c1 M_q M_k, every
+// logit (log2 units) is at most A - c2 D at distance D = i - j
+// (Cauchy-Schwarz on the content term) and every row's log-sum-exp is at
+// least its diagonal logit, so at least -A. P = exp2(logit - lse2) is then
+// below 2^(2A - c2 D), which rounds to an exact zero once c2 D > 2A + 152
+// (a margin of 2 over the 2^-150 rounding limit of fp32, and 2^-8 relative on
+// A, for the rounding of the products, of lse and of the bias). Zero P give
+// zero dV terms and zero dS, hence zero dK and dQ terms: a tile whose every
+// distance lies past that point adds exact zeros and is not visited.
+// norms: P partial maxima of the key norms of every pair, then those of the
+// query norms (nbh pairs each). Returns the largest distance that can still
+// carry a nonzero P, or 2^30 (nothing skipped).
+__device__ __forceinline__ int live_reach(const float* __restrict__ norms, int parts, int nbh, int bh, float c1,
+                                          float c2) {
+  if (norms == nullptr || !(c2 > 0.0f)) return 1 << 30;
+  float km = 0.0f, qm = 0.0f;
+  for (int p = 0; p < parts; ++p) {
+    km = fmaxf(km, norms[(long long)bh * parts + p]);
+    qm = fmaxf(qm, norms[((long long)nbh + bh) * parts + p]);
+  }
+  const float A = c1 * qm * km * (1.0f + 1.0f / 256.0f);
+  const float reach = (2.0f * A + 152.0f) / c2;  // dead: D > reach
+  return reach < 1.0e9f ? int(ceilf(reach)) : (1 << 30);
+}
+
 // ---------------------------------------------------------------- prep ------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
@@ -186,7 +212,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int H, int N, int nkb, int total,
-    const float* __restrict__ slopes, float c1, float scale, float clamp2) {
+    const float* __restrict__ slopes, float c1, float scale, float clamp2, const float* __restrict__ norms,
+    int parts) {
   static_assert(QB == 1 || QB == 2, "one or two 32-row query blocks per tile");
   constexpr int NT = 512, BK = 128, BQ = 32 * QB;
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
@@ -223,8 +250,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // per-lane byte offsets of the swizzled tile reads
   const int rb = Tile::row_base(lane), tb0 = Tile::tr_base(lane, 0), tb1 = Tile::tr_base(lane, 1);
 
-  const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? k0 / BQ : 0;
+  // Underflow skipping: queries more than R past a key give it P = 0 exactly,
+  // so the tiles whose first query lies past the block's last key + R (and
+  // all after them) are dropped, and a wave skips the tiles past its own keys'.
+  const int R = CAUSAL && VAR == 0 ? live_reach(norms, parts, total / nkb, bh, c1, c2) : (1 << 30);
+  int nqt = (N + BQ - 1) / BQ;
+  if (R < (1 << 30)) nqt = min(nqt, (k0 + BK - 1 + R) / BQ + 1);
 
   // staging registers of one query tile (NCH chunks of Q and of dO per thread)
   u32x4 rq[NCH], rdo[NCH];
@@ -409,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       if (t == nqt) return;
       const unsigned char* st = stage_of(t);
       const int q0 = t * BQ;
-      if (OPEN || !CAUSAL || q0 + BQ - 1 >= kw0) {
+      if (!CAUSAL || ((OPEN || q0 + BQ - 1 >= kw0) && q0 - (kw0 + 31) <= R)) {
         f32x16 p[QB];
         products(st, kf, cinit, p);
         const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
@@ -441,7 +473,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const unsigned char* st = stage_of(u);
       const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
       const int q0 = u * BQ;
-      if (!CAUSAL || q0 + BQ - 1 >= kw0) {
+      if (!CAUSAL || (q0 + BQ - 1 >= kw0 && q0 - (kw0 + 31) <= R)) {  // the dV wave's test
         f32x16 dp[QB];
         products(st + RBYTES, vf, f32x16{}, dp);
 #pragma unroll
@@ -483,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dq, int H, int N, int nqb, int total, const float* __restrict__ slopes,
-    float c1, float scale, float clamp2) {
+    float c1, float scale, float clamp2, const float* __restrict__ norms, int parts) {
   constexpr int NT = 256, BM = 128, BN = 32;
   constexpr int KS = D / 16, KB = BN / 32, DB = D / 32, PS = BN / 16, CPR = D / 8;
   using Tile = SwzTile<D>;              // K and V tiles: swizzled rows of 2 D bytes
@@ -536,6 +568,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
+  // Underflow skipping: key tiles whose last key lies more than R before the
+  // block's first query carry P = 0 exactly for every query of the block: the
+  // walk stops above them (t_lo), and a wave skips the tiles that far before
+  // its own first query.
+  const int R = CAUSAL && VAR == 0 ? live_reach(norms, parts, total / nqb, bh, c1, c2) : (1 << 30);
+  const int xdead = q0 - BN - R;  // tiles with j0 <= xdead are dead
+  const int t_lo = R < (1 << 30) && xdead >= 0 ? xdead / BN + 1 : 0;
 
   u32x4 rk[LOADS], rv[LOADS];
   // chunk tid + NT r of a tile: byte 16 (tid + NT r) past its first row; rows
@@ -574,11 +613,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     constexpr bool OPEN = decltype(open_tag)::value;
     const int j0 = tile * BN;
     __syncthreads();
-    if (tile > 0) load_tile(j0 - BN);
+    if (tile > t_lo) load_tile(j0 - BN);
     const unsigned char* st = smem + stage * STAGE;
     const unsigned char* sK = st;
     const unsigned char* sV = st + KBYTES;
-    const bool active = qw0 < N && (OPEN || !CAUSAL || j0 <= qw_last);
+    const bool active = qw0 < N && (!CAUSAL || ((OPEN || j0 <= qw_last) && qw0 - (j0 + BN - 1) <= R));
     if (active) {
       // ---- per 32-key block: S^T = K Q^T, dP^T = V dO^T (lane = query), then
       // P^T = exp2(t - lse2) and dS^T = P^T (dP^T - D) packed to bf16 ----
@@ -629,14 +668,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
           [&](int n) { return read_tr<D>(sK, tb0, tb1, 16 * (n % PS), 32 * (n / PS)); },
           [&](int n, const bf16x8& a) { acc[n / PS] = mfma32(a, __builtin_bit_cast(bf16x8, pf[n % PS]), acc[n / PS]); });
     }
-    if (tile > 0) store_tile(smem + (stage ^ 1) * STAGE);
+    if (tile > t_lo) store_tile(smem + (stage ^ 1) * STAGE);
     stage ^= 1;
   };
   const int x_open = q0 + 1;  // keys [0, x_open) are at or before every query of the block
   const int t_open = x_open < BN ? -1 : min(min(x_open / BN - 1, N / BN - 1), ntiles - 1);
   int tile = ntiles - 1;
-  for (; tile > t_open; --tile) step(tile, std::false_type{});
-  for (; tile >= 0; --tile) step(tile, std::true_type{});
+  for (; tile > max(t_open, t_lo - 1); --tile) step(tile, std::false_type{});
+  for (; tile >= t_lo; --tile) step(tile, std::true_type{});
 
   if (i < N) {
 #pragma unroll
@@ -684,12 +723,12 @@ hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, 
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VAR, 2>), dim3(unsigned(tk)), dim3(512), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
-                       nkb, int(tk), a.slopes, c1, scale, a.clamp2);
+                       nkb, int(tk), a.slopes, c1, scale, a.clamp2, a.norms, a.norm_parts);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VAR, 1>), dim3(unsigned(tk)), dim3(512), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
-                       nkb, int(tk), a.slopes, c1, scale, a.clamp2);
+                       nkb, int(tk), a.slopes, c1, scale, a.clamp2, a.norms, a.norm_parts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.N + 127) / 128;
@@ -697,7 +736,7 @@ hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, 
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VAR>), dim3(unsigned(tq)), dim3(256), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dq, a.H, a.N, nqb, int(tq),
-                     a.slopes, c1, scale, a.clamp2);
+                     a.slopes, c1, scale, a.clamp2, a.norms, a.norm_parts);
   return hipGetLastError();
 }
 

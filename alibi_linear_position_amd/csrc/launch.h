@@ -57,6 +57,11 @@ struct BwdArgs {
   int causal;
   int flags = 0;         // ALIBI_CLAMP | ALIBI_LOG_DISTANCE: the bias-only mitigations
   float clamp2 = 0.0f;   // bias floor in log2 units (ALIBI_CLAMP)
+  // exact underflow skipping (plain causal form): P partial maxima of the key
+  // norms of every (b, h), then those of the query norms (launch_knorm_max),
+  // or null for no skipping
+  const float* norms = nullptr;
+  int norm_parts = 0;
 };
 
 // Backward, d in {64, 128}; ws holds 2 B H N floats (D and lse in log2 units).

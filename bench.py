@@ -151,7 +151,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd16k", "c1", "c2", "c3", "decode", "copy", "bwd", "mfma",
+    ap.add_argument("--only", choices=["fwd", "fwd16k", "c1", "c2", "c3", "decode", "copy", "bwd", "bwd_skip", "mfma",
                                        "mfma_valu", "oracle", "underflow"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -374,6 +374,21 @@ def next_forms(alibi, q, k, v, s, fw):
     ms = time_launches(lambda: alibi.attn_bwd(q, k, v, out, dout, lse, s, True), warmup=5, reps=10)
     res["backward"] = {"value": round(2.5 * causal_flops / ms / 1e9, 1), "unit": "TFLOP/s", "ms": round(ms, 4),
                        "note": "dq, dk, dv; flops = 5 causal GEMMs (S, dP, dV, dK, dQ) = 2.5x the forward's"}
+    grads = []
+
+    def bwd_skip():
+        grads[:] = alibi.attn_bwd(q, k, v, out, dout, lse, s, True, skip_underflow=True)
+
+    ms = time_launches(bwd_skip, warmup=5, reps=10)
+    ref = alibi.attn_bwd(q, k, v, out, dout, lse, s, True)
+    torch.cuda.synchronize()
+    same = all(bool(torch.equal(a.view(torch.int16), b.view(torch.int16))) for a, b in zip(grads, ref))
+    res["backward_skip_underflow"] = {
+        "value": round(2.5 * causal_flops / ms / 1e9, 1), "unit": "TFLOP/s (unskipped causal flops)",
+        "ms": round(ms, 4), "bitwise_equal_to_backward": same,
+        "note": "exact skipping of query-key tiles whose every P rounds to zero (bound from the per-(b,h) "
+                "maxima of |q| and |k|, whose pass is included); flops are the unskipped count, so this is "
+                "an effective rate"}
     lse2 = torch.empty_like(lse)
     out2 = torch.empty_like(q)
     alibi.attn_fwd_ex(q, k, v, s, True, out=out2, lse=lse2, clamp=-87.0, log_distance=True)
@@ -625,13 +640,14 @@ def run_only(args, alibi, W, fw, dw, dev):
         s = alibi.slopes(dw.H).to(dev)
         fn = lambda: alibi.attn_decode(qd, kc, vc, s, out=od)
         work, unit = decode_bytes(dw.B, dw.H, dw.L, dw.d), "B"
-    elif args.only == "bwd":
+    elif args.only in ("bwd", "bwd_skip"):
         q, k, v = (x.to(dev) for x in W.gaussian_qkv_bf16(fw.shape, seed=fw.seed))
         s = alibi.slopes(fw.H).to(dev)
         out, lse = alibi.attn_fwd_train(q, k, v, s, True)
         dout = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev,
                            dtype=torch.float32).to(torch.bfloat16)
-        fn = lambda: alibi.attn_bwd(q, k, v, out, dout, lse, s, True)
+        skip = args.only == "bwd_skip"
+        fn = lambda: alibi.attn_bwd(q, k, v, out, dout, lse, s, True, skip_underflow=skip)
         work, unit = 2.5 * fwd_flops(fw.B, fw.H, fw.N, fw.d), "flop"
     elif args.only in ("mfma", "mfma_valu"):
         lib = alibi.load_library()

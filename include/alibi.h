@@ -311,8 +311,18 @@ int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out,
  * bias. lse must come from alibi_attn_fwd_ex with the same opts. Everything
  * else as alibi_attn_bwd (which is this call with opts = NULL).
  * ALIBI_SOFTCAP, ALIBI_WINDOW and nonzero offsets: ALIBI_ENOTSUP (forward-only
- * forms); ALIBI_SKIP_UNDERFLOW is ignored; unknown bits or a non-finite
- * clamp: ALIBI_EINVAL.
+ * forms); unknown bits or a non-finite clamp: ALIBI_EINVAL.
+ * ALIBI_SKIP_UNDERFLOW (plain causal form; accepted and without effect with
+ * the mitigations or without the causal mask): a first pass takes max|q_i|
+ * and max|k_j| per (b, h); every logit is then at most A - m D (A =
+ * max|q| max|k| / sqrt(d)) and every row's log-sum-exp at least -A (its
+ * diagonal logit), so query-key pairs further apart than D with
+ * m D log2(e) > 2 A log2(e) + 152 have P = exp(logit - lse) rounding to an
+ * exact zero, and so add exact zeros to dq, dk and dv: the tiles made only of
+ * such pairs are not visited. For finite inputs and lse from the matching
+ * forward the gradients are bit-identical to the call without the flag. The
+ * workspace then also holds 2 B H P floats of norm maxima (P <= 2048 / (B H)
+ * rounded up, at least 1).
  */
 int alibi_attn_bwd_ex(const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv,

@@ -388,7 +388,7 @@ def test_bwd_ex_validation(lib):
 
     assert bwd_ex(None) == -3
     for flags in (alibi.CLAMP, alibi.LOG_DISTANCE, alibi.CLAMP | alibi.LOG_DISTANCE,
-                  alibi.CLAMP | alibi.SKIP_UNDERFLOW):
+                  alibi.CLAMP | alibi.SKIP_UNDERFLOW, alibi.SKIP_UNDERFLOW):
         assert bwd_ex(O(flags, -87.0, 0.0, 0, 0)) == -3, flags
         assert bwd_ex(O(flags, -87.0, 0.0, 0, 0), causal=0, d=128) == -3, flags
     assert bwd_ex(O(alibi.CLAMP, float("nan"), 0.0, 0, 0)) == -1          # clamp not finite
