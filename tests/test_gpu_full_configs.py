@@ -1,10 +1,10 @@
 """Every element of the large configurations against the fp64 oracle (needs an MI355X).
 
 The 16384-token forward (B1 H16 d128), the N = 4096, d = 128 forward the
-benchmark times (B8 H16), the 32768-token decode (B32 H32 d128) and the backward
-at the benchmark's sequence shape (B1 H16 N4096 d128) are compared element by
-element, one (b, h) at a time so that the oracle's (N, N) matrices stay within
-host memory. The kernels run in the launch configuration bench.py times (the
+benchmark times (B8 H16) and the 32768-token decode (B32 H32 d128) are compared
+element by element, one (b, h) at a time so that the oracle's (N, N) matrices
+stay within host memory (the backward at the benchmark's sequence shape,
+B1 H16 N4096 d128, is compared the same way in test_gpu_backward.py). The kernels run in the launch configuration bench.py times (the
 library's automatic choice). Tolerances as in tests/parity_util.py and
 tests/test_gpu_backward.py.
 """
