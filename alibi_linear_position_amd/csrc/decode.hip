@@ -65,8 +65,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   const int tid = threadIdx.x;
   const int g = tid / LPK;
   const int sub = tid % LPK;
-  const long long bh = blockIdx.x / splits;
-  const int s = int(blockIdx.x - bh * splits);
+  // Workgroup -> (key range, head, batch), the newest range first. With the
+  // exact skipping only the ranges near the query hold work, most of it in
+  // the shallow heads; in this order consecutive workgroups, which are dealt
+  // to the 8 XCDs round-robin, take the batches of one (range, head), so that
+  // work spreads over every XCD (in pair-major order, with 4 ranges per pair,
+  // range s of every pair fell on XCDs s and s + 4). The plain decode runs
+  // equally fast in either order.
+  const long long nbh = gridDim.x / splits;
+  const int nb = int(nbh / H);
+  const long long w = blockIdx.x;
+  const int s = splits - 1 - int(w / nbh);
+  const long long bh = (w % nb) * H + (w / nb) % H;
   const int h = int(bh % H);
   const float c2 = slopes[h] * kLog2e;
   const int jbeg = s * chunk;
