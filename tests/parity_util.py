@@ -9,6 +9,8 @@
 import numpy as np
 import torch
 
+import oracle
+
 BF16_TOL = 1e-2
 F32_TOL = 1e-5
 U_BF16 = 2.0 ** -8  # unit roundoff of bf16: 8 significant bits, round to nearest even
@@ -16,6 +18,10 @@ U_BF16 = 2.0 ** -8  # unit roundoff of bf16: 8 significant bits, round to neares
 # bf16-rounded weights, a sum of positive terms each within relative U_BF16, so
 # |err| <= ln(1 + 2^-8) = 3.90e-3 plus fp32 rounding.
 LSE_TOL = 4e-3
+# Gradients: |gpu - o| <= G_ATOL + G_RTOL (|o| + M) + E per element, the bar
+# derived in tests/test_gpu_backward.py.
+G_ATOL = 1e-2
+G_RTOL = 1e-2
 
 
 def o_rounding_bound(p, o, q, k, do):
@@ -83,3 +89,27 @@ class Bf16Stats:
 
 def dev(x):
     return x.to("cuda").contiguous()
+
+
+def check_grad(gpu, ref, label, mag=None, extra=0.0):
+    """mag: the oracle's magnitude sums for these elements (None: |ref| bounds them);
+    extra: the bound E on the effect of the output's bf16 rounding."""
+    g = gpu.detach().to("cpu", torch.float64).numpy()
+    err = np.abs(g - ref)
+    m = np.abs(ref) if mag is None else np.asarray(mag)
+    bar = G_ATOL + G_RTOL * (np.abs(ref) + m) + extra
+    bad = int(np.sum(err > bar))
+    over_old = int(np.sum(err > G_ATOL + G_RTOL * np.abs(ref)))
+    print(f"[parity] {label}: max|err|={err.max():.3e} max|ref|={np.abs(ref).max():.3e} "
+          f"max err/bar={np.max(err / bar):.3f} beyond 1e-2+1e-2|o|: {over_old} failing={bad}", flush=True)
+    assert np.all(np.isfinite(g)) and bad == 0, label
+
+
+def check_grads(gpu3, q, k, v, do, m, causal, label, clamp=None, log_distance=False):
+    """dq, dk, dv of one head (bf16 tensors) against the fp64 oracle's chain rule."""
+    (rq, rk, rv), (mq, mk, mv) = oracle.attn_backward_head_ref(q, k, v, do, m, causal, magnitudes=True,
+                                                               clamp=clamp, log_distance=log_distance)
+    o, p = oracle.variant_head_ref(q, k, v, m, causal, clamp=clamp, log_distance=log_distance)
+    eq, ek = o_rounding_bound(p, o, *(x.double().numpy() for x in (q, k, do)))
+    for g, r, mg, e, n in zip(gpu3, (rq, rk, rv), (mq, mk, mv), (eq, ek, 0.0), ("dq", "dk", "dv")):
+        check_grad(g, r, f"{n} {label}", mg, e)

@@ -26,41 +26,15 @@ import torch
 
 import oracle
 import workloads as W
-from parity_util import F32_TOL, LSE_TOL, dev, o_rounding_bound
+from parity_util import F32_TOL, LSE_TOL, check_grad, check_grads, dev
 
 pytestmark = pytest.mark.gpu
-
-G_ATOL = 1e-2
-G_RTOL = 1e-2
 
 @pytest.fixture(scope="module")
 def alibi():
     import alibi_linear_position_amd as mod
     mod.load_library()
     return mod
-
-
-def check_grad(gpu, ref, label, mag=None, extra=0.0):
-    """mag: the oracle's magnitude sums for these elements (None: |ref| bounds them);
-    extra: the bound E on the effect of the output's bf16 rounding."""
-    g = gpu.detach().to("cpu", torch.float64).numpy()
-    err = np.abs(g - ref)
-    m = np.abs(ref) if mag is None else np.asarray(mag)
-    bar = G_ATOL + G_RTOL * (np.abs(ref) + m) + extra
-    bad = int(np.sum(err > bar))
-    over_old = int(np.sum(err > G_ATOL + G_RTOL * np.abs(ref)))
-    print(f"[parity] {label}: max|err|={err.max():.3e} max|ref|={np.abs(ref).max():.3e} "
-          f"max err/bar={np.max(err / bar):.3f} beyond 1e-2+1e-2|o|: {over_old} failing={bad}", flush=True)
-    assert np.all(np.isfinite(g)) and bad == 0, label
-
-
-def check_grads(gpu3, q, k, v, do, m, causal, label, clamp=None, log_distance=False):
-    (rq, rk, rv), (mq, mk, mv) = oracle.attn_backward_head_ref(q, k, v, do, m, causal, magnitudes=True,
-                                                               clamp=clamp, log_distance=log_distance)
-    o, p = oracle.variant_head_ref(q, k, v, m, causal, clamp=clamp, log_distance=log_distance)
-    eq, ek = o_rounding_bound(p, o, *(x.double().numpy() for x in (q, k, do)))
-    for g, r, mg, e, n in zip(gpu3, (rq, rk, rv), (mq, mk, mv), (eq, ek, 0.0), ("dq", "dk", "dv")):
-        check_grad(g, r, f"{n} {label}", mg, e)
 
 
 def _inputs(shape, seed):

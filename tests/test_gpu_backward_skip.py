@@ -17,8 +17,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity_util import dev
-from test_gpu_backward import check_grads
+from parity_util import check_grads, dev
 
 pytestmark = pytest.mark.gpu
 
