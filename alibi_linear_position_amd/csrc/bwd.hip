@@ -34,6 +34,11 @@
 // Sec. 3.4 mitigations, B = max(-m D*, c), D* = D or ln(D + 1): both change
 // only the constant bias, so the rest of the chain rule is the same. The
 // scores are then not seeded and the bias is formed per score.
+//
+// With the per-(b, h) norm maxima of Q and K (plain causal form), both
+// kernels end their walks, and each wave skips its own tiles, at the distance
+// past which every P is an exact zero (live_reach below): the gradients keep
+// every bit.
 #include "device_common.h"
 #include "launch.h"
 
