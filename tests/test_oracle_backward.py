@@ -167,6 +167,63 @@ def test_backward_mitigations_match_finite_differences(clamp, logd):
         assert np.allclose(grad, num, atol=1e-7), which
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("z,clamp,logd", [(2.0, None, False), (1.5, -2.0, True), (4.0, None, True)])
+def test_backward_softcap_matches_autograd(causal, z, clamp, logd):
+    # autograd through z tanh(q k / sqrt(d) / z) plus a constant bias; the
+    # bias is what the pinned forward oracle's weights leave once its capped
+    # content logits are taken away (log w + lse - z tanh(A / z)). Small z
+    # keeps tanh well away from linear, so a missing or wrong 1 - tanh^2
+    # factor fails.
+    import torch
+    n, d, m = 19, 16, 0.5
+    q, k, v, do = (_rand((n, d), s, 1.5) for s in (51, 52, 53, 54))
+    _, w = oracle.variant_head_ref(q, k, v, m, causal, clamp, logd, softcap=z)
+    lse = oracle.lse_head_ref(q, k, m, causal, clamp, logd, softcap=z)
+    a = q @ k.T / math.sqrt(d)
+    with np.errstate(divide="ignore"):
+        bias = np.log(w) + lse[:, None] - z * np.tanh(a / z)
+    qt, kt, vt = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    logits = z * torch.tanh(qt @ kt.T / math.sqrt(d) / z) + torch.tensor(bias)
+    out = torch.softmax(logits, dim=-1) @ vt
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    got = oracle.attn_backward_head_ref(q, k, v, do, m, causal, clamp=clamp, log_distance=logd, softcap=z)
+    for g, x in zip(got, (qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy())):
+        assert np.allclose(g, x, atol=1e-11, rtol=1e-9)
+
+
+@pytest.mark.parametrize("z,logd", [(1.0, False), (2.5, True)])
+def test_backward_softcap_matches_finite_differences(z, logd):
+    n, d, m, eps = 6, 4, 0.8, 1e-6
+    q, k, v, do = (_rand((n, d), s, 1.2) for s in (55, 56, 57, 58))
+    dq, dk, dv = oracle.attn_backward_head_ref(q, k, v, do, m, True, log_distance=logd, softcap=z)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.variant_head_ref(qq, kk, vv, m, True, None, logd, softcap=z)
+        return float(np.sum(o * do))
+
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            plus = [q.copy(), k.copy(), v.copy()]
+            minus = [q.copy(), k.copy(), v.copy()]
+            plus[which][idx] += eps
+            minus[which][idx] -= eps
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * eps)
+        assert np.allclose(grad, num, atol=1e-7), which
+
+
+def test_backward_large_softcap_is_the_uncapped_head():
+    # z tanh(A / z) = A - A^3 / (3 z^2) + ...: at z = 1e6 the capped gradients
+    # agree with the plain ones to ~1e-12 relative
+    q, k, v, do = (_rand((17, 8), s) for s in (59, 60, 61, 62))
+    for causal in (True, False):
+        got = oracle.attn_backward_head_ref(q, k, v, do, 0.3, causal, softcap=1e6)
+        want = oracle.attn_backward_head_ref(q, k, v, do, 0.3, causal)
+        for g, x in zip(got, want):
+            assert np.allclose(g, x, atol=1e-9, rtol=1e-9)
+
+
 def test_backward_clamp_above_every_bias_is_the_slope_free_head():
     # a floor at 0 lifts every bias -m D <= 0 to 0: the gradients of m = 0
     q, k, v, do = (_rand((15, 8), s) for s in (39, 40, 41, 42))
