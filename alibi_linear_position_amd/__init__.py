@@ -262,11 +262,12 @@ def attn_fwd_train(q, k, v, slopes=None, causal=True):
 
 
 def attn_bwd(q, k, v, out, dout, lse, slopes=None, causal=True, clamp=None, log_distance=False,
-             skip_underflow=False):
+             skip_underflow=False, softcap=None):
     """Gradients (dq, dk, dv), bf16 (B, H, N, d), of the plain forward, or of the
-    forward with the clamp and/or log-distance bias (lse from attn_fwd_ex with
-    the same settings). skip_underflow: exact skipping of the query-key tiles
-    whose every P rounds to zero (plain causal form; bit-identical gradients)."""
+    forward with the clamp, the log-distance bias and/or the soft cap z (lse from
+    attn_fwd_ex with the same settings). skip_underflow: exact skipping of the
+    query-key tiles whose every P rounds to zero (plain causal form;
+    bit-identical gradients)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _need(t, torch.bfloat16, 4, n)
@@ -279,11 +280,12 @@ def attn_bwd(q, k, v, out, dout, lse, slopes=None, causal=True, clamp=None, log_
     s = _slopes_dev(slopes, H, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     o = None
-    if clamp is not None or log_distance or skip_underflow:
+    if clamp is not None or log_distance or skip_underflow or softcap is not None:
         o = FwdOpts()
         o.flags = ((CLAMP if clamp is not None else 0) | (LOG_DISTANCE if log_distance else 0)
-                   | (SKIP_UNDERFLOW if skip_underflow else 0))
+                   | (SKIP_UNDERFLOW if skip_underflow else 0) | (SOFTCAP if softcap is not None else 0))
         o.clamp_min = float(clamp) if clamp is not None else 0.0
+        o.softcap = float(softcap) if softcap is not None else 0.0
     with torch.cuda.device(q.device):
         st = load_library().alibi_attn_bwd_ex(
             _P(q.data_ptr()), _P(k.data_ptr()), _P(v.data_ptr()), _P(out.data_ptr()),

@@ -231,17 +231,19 @@ int alibi_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o
   if (lse == nullptr || !aligned(lse, 4)) return ALIBI_EINVAL;
   if (causal != 0 && causal != 1) return ALIBI_EINVAL;
   int flags = 0;
-  float clamp_min = 0.0f;
+  float clamp_min = 0.0f, softcap = 0.0f;
   bool skip = false;
   if (opts != nullptr) {
     if ((opts->flags & ~(ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP | ALIBI_SKIP_UNDERFLOW | ALIBI_WINDOW)) != 0)
       return ALIBI_EINVAL;
     if ((opts->flags & ALIBI_CLAMP) && !std::isfinite(opts->clamp_min)) return ALIBI_EINVAL;
-    // the soft cap, the window and position offsets are forward-only forms
-    if ((opts->flags & (ALIBI_SOFTCAP | ALIBI_WINDOW)) != 0 || opts->q_offset != 0 || opts->k_offset != 0)
-      return ALIBI_ENOTSUP;
-    flags = opts->flags & (ALIBI_CLAMP | ALIBI_LOG_DISTANCE);
+    if ((opts->flags & ALIBI_SOFTCAP) && !(std::isfinite(opts->softcap) && opts->softcap > 0.0f))
+      return ALIBI_EINVAL;
+    // the window and position offsets are forward-only forms
+    if ((opts->flags & ALIBI_WINDOW) != 0 || opts->q_offset != 0 || opts->k_offset != 0) return ALIBI_ENOTSUP;
+    flags = opts->flags & (ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP);
     clamp_min = opts->clamp_min;
+    softcap = opts->softcap;
     skip = (opts->flags & ALIBI_SKIP_UNDERFLOW) != 0;
   }
   if (d != 64 && d != 128) return ALIBI_ENOTSUP;
@@ -263,6 +265,10 @@ int alibi_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o
   alibi::BwdArgs a{q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, slopes, causal};
   a.flags = flags;
   a.clamp2 = clamp_min * 1.4426950408889634f;  // as the forward forms its floor (log2 units)
+  if (flags & ALIBI_SOFTCAP) {                  // as the forward forms its cap
+    a.cap_in = float(2.0 * double(scale_log2(d)) / double(softcap));
+    a.cap_out = float(double(softcap) * 1.4426950408889634);
+  }
   if (skip) {
     float* norms = ws + (size_t)2 * B * H * N;
     st = hip_status(alibi::launch_knorm_max(k, norms, B, H, N, d, parts, stream));

@@ -30,10 +30,13 @@
 // Scores are in log2 units (c1 = log2(e) / sqrt(d), c2 = m log2(e)); masked and
 // out-of-range entries get P = 0.
 //
-// VAR (bits 1: clamp, 2: log distance) recomputes P with the bias of those
-// Sec. 3.4 mitigations, B = max(-m D*, c), D* = D or ln(D + 1): both change
-// only the constant bias, so the rest of the chain rule is the same. The
-// scores are then not seeded and the bias is formed per score.
+// VAR (bits 1: clamp, 2: log distance, 4: soft cap) recomputes P with the
+// logits of those Sec. 3.4 mitigations: B = max(-m D*, c), D* = D or
+// ln(D + 1), change only the constant bias, so the rest of the chain rule is
+// the same; the soft cap A* = z tanh(A / z) of the content logit adds the
+// factor dA*/dA = 1 - tanh(A / z)^2 to dS before dQ and dK (the dV waves hand
+// P (1 - tanh^2) to the dK waves, and the dQ kernel scales its dS). The
+// scores are then not seeded and the logit is formed per score.
 //
 // With the per-(b, h) norm maxima of Q and K (plain causal form), both
 // kernels end their walks, and each wave skips its own tiles, at the distance
@@ -51,7 +54,7 @@ namespace alibi {
 
 namespace {
 
-constexpr int kBwdClamp = 1, kBwdLog = 2;
+constexpr int kBwdClamp = 1, kBwdLog = 2, kBwdCap = 4;
 
 // Bias of distance D >= 0 in log2 units for the VAR forms.
 template <int VAR>
@@ -64,6 +67,14 @@ __device__ __forceinline__ float var_bias(float dd, float c2, float mh, float cl
   }
   if constexpr ((VAR & kBwdClamp) != 0) b = fmaxf(b, clamp2);
   return b;
+}
+
+// Soft-capped content logit in log2 units from the raw score s = q.k:
+// z log2(e) tanh(A / z) = cap_out (1 - 2 / (e^(2 A / z) + 1)) with
+// e^(2 A / z) = exp2(s cap_in); th = tanh(A / z), for dA*/dA = 1 - th^2.
+__device__ __forceinline__ float cap_logit(float s, float cap_in, float cap_out, float& th) {
+  th = fmaf(-2.0f, __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(s * cap_in) + 1.0f), 1.0f);
+  return cap_out * th;
 }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -217,9 +228,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int H, int N, int nkb, int total,
-    const float* __restrict__ slopes, float c1, float scale, float clamp2, const float* __restrict__ norms,
-    int parts) {
+    const float* __restrict__ slopes, float c1, float scale, float clamp2, float cap_in, float cap_out,
+    const float* __restrict__ norms, int parts) {
   static_assert(QB == 1 || QB == 2, "one or two 32-row query blocks per tile");
+  constexpr bool CAP = (VAR & kBwdCap) != 0;
   constexpr int NT = 512, BK = 128, BQ = 32 * QB;
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
   using Tile = SwzTile<D>;             // Q / dO tiles: swizzled rows of 2 D bytes
@@ -324,7 +336,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         [&](int n, const bf16x8& a) { out[n % QB] = mfma32(a, kf[n / QB], out[n % QB]); });
   };
   // P = exp2(t - lse2) of block b of a tile whose first row is q0
-  auto probs = [&](f32x16& s, const float* sL, int q0, auto open_tag) {
+  // with the soft cap, gc receives dA*/dA = 1 - tanh^2 per score
+  auto probs = [&](f32x16& s, const float* sL, int q0, auto open_tag, f32x16& gc) {
     constexpr bool OPEN = decltype(open_tag)::value;  // no query of the tile precedes a key of the block
     const float bj = c2 * float(j - q0 - 4 * hi);  // t = s c1 + bj on the causal side
     const bool full = OPEN || (CAUSAL && q0 >= kw0 + 31);  // every query of the block sees every key of the wave
@@ -339,6 +352,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         if constexpr (VAR == 0) {
           t = fmaf(s[r], c1, bj);
           if (!OPEN && !full && !CAUSAL && j > i) t -= 2.0f * c2 * float(j - i);  // symmetric bias -m |i - j|
+        } else if constexpr (CAP) {
+          float th;
+          t = cap_logit(s[r], cap_in, cap_out, th) +
+              var_bias<VAR>(float(CAUSAL ? max(i - j, 0) : abs(i - j)), c2, mh, clamp2);
+          gc[r] = fmaf(-th, th, 1.0f);
         } else {
           t = fmaf(s[r], c1, var_bias<VAR>(float(CAUSAL ? max(i - j, 0) : abs(i - j)), c2, mh, clamp2));
         }
@@ -447,15 +465,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const unsigned char* st = stage_of(t);
       const int q0 = t * BQ;
       if (!CAUSAL || ((OPEN || q0 + BQ - 1 >= kw0) && q0 - (kw0 + 31) <= R)) {
-        f32x16 p[QB];
+        f32x16 p[QB], gcap[QB];
         products(st, kf, cinit, p);
         const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
-          probs(p[b], sL + 32 * b, q0 + 32 * b, open_tag);
-          put_p(p_slot(t, b), p[b]);
+          probs(p[b], sL + 32 * b, q0 + 32 * b, open_tag, gcap[b]);
+          if constexpr (!CAP) put_p(p_slot(t, b), p[b]);
         }
         accumulate(st + RBYTES, p);
+        if constexpr (CAP) {
+          // the dK waves form dS = P (1 - tanh^2) (dP - D)
+#pragma unroll
+          for (int b = 0; b < QB; ++b) {
+            p[b] *= gcap[b];
+            put_p(p_slot(t, b), p[b]);
+          }
+        }
       }
       stage_next(t);
     };
@@ -520,8 +546,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dq, int H, int N, int nqb, int total, const float* __restrict__ slopes,
-    float c1, float scale, float clamp2, const float* __restrict__ norms, int parts) {
+    float c1, float scale, float clamp2, float cap_in, float cap_out, const float* __restrict__ norms, int parts) {
   constexpr int NT = 256, BM = 128, BN = 32;
+  constexpr bool CAP = (VAR & kBwdCap) != 0;
   constexpr int KS = D / 16, KB = BN / 32, DB = D / 32, PS = BN / 16, CPR = D / 8;
   using Tile = SwzTile<D>;              // K and V tiles: swizzled rows of 2 D bytes
   constexpr int KBYTES = BN * Tile::ROWB;
@@ -647,7 +674,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * half + e;
-            float t;
+            float t, th = 0.0f;
             if constexpr (VAR == 0) {
               t = fmaf(s[r], c1, bt0 + 32.0f * kb * c2);
               if (!OPEN && !full) {
@@ -655,12 +682,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 if (!CAUSAL && jj > i) t -= 2.0f * c2 * float(jj - i);
                 if (jj >= N || (CAUSAL && jj > i)) t = -__builtin_huge_valf();
               }
+            } else if constexpr (CAP) {
+              const int jj = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+              t = cap_logit(s[r], cap_in, cap_out, th) +
+                  (var_bias<VAR>(float(CAUSAL ? max(i - jj, 0) : abs(i - jj)), c2, mh, clamp2) - L);
+              if (!OPEN && !full && (jj >= N || (CAUSAL && jj > i))) t = -__builtin_huge_valf();
             } else {
               const int jj = j0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
               t = fmaf(s[r], c1, var_bias<VAR>(float(CAUSAL ? max(i - jj, 0) : abs(i - jj)), c2, mh, clamp2) - L);
               if (!OPEN && !full && (jj >= N || (CAUSAL && jj > i))) t = -__builtin_huge_valf();
             }
-            x[e] = fast_exp2(t) * dp[r];
+            if constexpr (CAP)
+              x[e] = fast_exp2(t) * fmaf(-th, th, 1.0f) * dp[r];  // dS of the content logit
+            else
+              x[e] = fast_exp2(t) * dp[r];
           }
           u32x4 pk;
 #pragma unroll
@@ -728,12 +763,12 @@ hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, 
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VAR, 2>), dim3(unsigned(tk)), dim3(512), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
-                       nkb, int(tk), a.slopes, c1, scale, a.clamp2, a.norms, a.norm_parts);
+                       nkb, int(tk), a.slopes, c1, scale, a.clamp2, a.cap_in, a.cap_out, a.norms, a.norm_parts);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VAR, 1>), dim3(unsigned(tk)), dim3(512), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.N,
-                       nkb, int(tk), a.slopes, c1, scale, a.clamp2, a.norms, a.norm_parts);
+                       nkb, int(tk), a.slopes, c1, scale, a.clamp2, a.cap_in, a.cap_out, a.norms, a.norm_parts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.N + 127) / 128;
@@ -741,7 +776,7 @@ hipError_t launch_bwd_cfg(const BwdArgs& a, float* dsum, float* lse2, float c1, 
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VAR>), dim3(unsigned(tq)), dim3(256), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, lse2, dsum, (uint16_t*)a.dq, a.H, a.N, nqb, int(tq),
-                     a.slopes, c1, scale, a.clamp2, a.norms, a.norm_parts);
+                     a.slopes, c1, scale, a.clamp2, a.cap_in, a.cap_out, a.norms, a.norm_parts);
   return hipGetLastError();
 }
 
@@ -751,11 +786,15 @@ namespace {
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_var(const BwdArgs& a, float* dsum, float* lse2, float c1, hipStream_t stream) {
-  switch (a.flags & 3) {
+  switch (a.flags & 7) {
     case 0: return launch_bwd_cfg<D, CAUSAL, 0>(a, dsum, lse2, c1, stream);
     case 1: return launch_bwd_cfg<D, CAUSAL, 1>(a, dsum, lse2, c1, stream);
     case 2: return launch_bwd_cfg<D, CAUSAL, 2>(a, dsum, lse2, c1, stream);
-    default: return launch_bwd_cfg<D, CAUSAL, 3>(a, dsum, lse2, c1, stream);
+    case 3: return launch_bwd_cfg<D, CAUSAL, 3>(a, dsum, lse2, c1, stream);
+    case 4: return launch_bwd_cfg<D, CAUSAL, 4>(a, dsum, lse2, c1, stream);
+    case 5: return launch_bwd_cfg<D, CAUSAL, 5>(a, dsum, lse2, c1, stream);
+    case 6: return launch_bwd_cfg<D, CAUSAL, 6>(a, dsum, lse2, c1, stream);
+    default: return launch_bwd_cfg<D, CAUSAL, 7>(a, dsum, lse2, c1, stream);
   }
 }
 

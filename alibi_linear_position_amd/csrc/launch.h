@@ -55,8 +55,12 @@ struct BwdArgs {
   int B, H, N, d;
   const float* slopes;
   int causal;
-  int flags = 0;         // ALIBI_CLAMP | ALIBI_LOG_DISTANCE: the bias-only mitigations
+  int flags = 0;         // ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP
   float clamp2 = 0.0f;   // bias floor in log2 units (ALIBI_CLAMP)
+  // soft cap z (ALIBI_SOFTCAP): exp2(s cap_in) = e^(2 A / z) for the raw score
+  // s = q.k, and the capped logit z tanh(A / z) in log2 units is cap_out tanh(A / z)
+  float cap_in = 0.0f;
+  float cap_out = 0.0f;
   // exact underflow skipping (plain causal form): P partial maxima of the key
   // norms of every (b, h), then those of the query norms (launch_knorm_max),
   // or null for no skipping

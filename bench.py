@@ -397,6 +397,11 @@ def next_forms(alibi, q, k, v, s, fw):
     res["backward_clamp+log"] = {"value": round(2.5 * causal_flops / ms / 1e9, 1), "unit": "TFLOP/s",
                                  "ms": round(ms, 4),
                                  "note": "the backward of the clamp (-87) with log-scaled distances; bias per score"}
+    alibi.attn_fwd_ex(q, k, v, s, True, out=out2, lse=lse2, softcap=50.0)
+    ms = time_launches(lambda: alibi.attn_bwd(q, k, v, out2, dout, lse2, s, True, softcap=50.0), warmup=5, reps=10)
+    res["backward_softcap"] = {"value": round(2.5 * causal_flops / ms / 1e9, 1), "unit": "TFLOP/s",
+                               "ms": round(ms, 4),
+                               "note": "the backward of the soft cap z = 50: tanh per score, dS scaled by 1 - tanh^2"}
     nq = 512
     qc = q[:, :, N - nq:].contiguous()
     oc = torch.empty_like(qc)

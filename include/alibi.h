@@ -303,15 +303,18 @@ int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                    hipStream_t stream);
 
 /*
- * Backward pass of the forward with the bias-only mitigations of Sec. 3.4 of
- * "When Attention Goes Blind" (the paper trains with them): opts->flags may
- * hold ALIBI_CLAMP (opts->clamp_min, finite) and ALIBI_LOG_DISTANCE, which
- * change only the constant bias, B = max(-m D*, c) with D* = D or ln(D + 1),
- * so the gradients follow the same chain rule with P recomputed under that
- * bias. lse must come from alibi_attn_fwd_ex with the same opts. Everything
- * else as alibi_attn_bwd (which is this call with opts = NULL).
- * ALIBI_SOFTCAP, ALIBI_WINDOW and nonzero offsets: ALIBI_ENOTSUP (forward-only
- * forms); unknown bits or a non-finite clamp: ALIBI_EINVAL.
+ * Backward pass of the forward with the mitigations of Sec. 3.4 of "When
+ * Attention Goes Blind" (the paper trains with them): opts->flags may hold
+ * ALIBI_CLAMP (opts->clamp_min, finite) and ALIBI_LOG_DISTANCE, which change
+ * only the constant bias, B = max(-m D*, c) with D* = D or ln(D + 1), so the
+ * gradients follow the same chain rule with P recomputed under that bias; and
+ * ALIBI_SOFTCAP (opts->softcap = z, finite and > 0), whose capped content
+ * logit z tanh(A / z) adds the factor 1 - tanh(A / z)^2 to dS before dQ and dK
+ * are formed. lse must come from alibi_attn_fwd_ex with the same opts.
+ * Everything else as alibi_attn_bwd (which is this call with opts = NULL).
+ * ALIBI_WINDOW and nonzero offsets: ALIBI_ENOTSUP (forward-only forms);
+ * unknown bits, a non-finite clamp or a soft cap that is not finite and
+ * positive: ALIBI_EINVAL.
  * ALIBI_SKIP_UNDERFLOW (plain causal form; accepted and without effect with
  * the mitigations or without the causal mask): a first pass takes max|q_i|
  * and max|k_j| per (b, h); every logit is then at most A - m D (A =

@@ -105,11 +105,12 @@ def check_grad(gpu, ref, label, mag=None, extra=0.0):
     assert np.all(np.isfinite(g)) and bad == 0, label
 
 
-def check_grads(gpu3, q, k, v, do, m, causal, label, clamp=None, log_distance=False):
+def check_grads(gpu3, q, k, v, do, m, causal, label, clamp=None, log_distance=False, softcap=None):
     """dq, dk, dv of one head (bf16 tensors) against the fp64 oracle's chain rule."""
     (rq, rk, rv), (mq, mk, mv) = oracle.attn_backward_head_ref(q, k, v, do, m, causal, magnitudes=True,
-                                                               clamp=clamp, log_distance=log_distance)
-    o, p = oracle.variant_head_ref(q, k, v, m, causal, clamp=clamp, log_distance=log_distance)
+                                                               clamp=clamp, log_distance=log_distance,
+                                                               softcap=softcap)
+    o, p = oracle.variant_head_ref(q, k, v, m, causal, clamp=clamp, log_distance=log_distance, softcap=softcap)
     eq, ek = o_rounding_bound(p, o, *(x.double().numpy() for x in (q, k, do)))
     for g, r, mg, e, n in zip(gpu3, (rq, rk, rv), (mq, mk, mv), (eq, ek, 0.0), ("dq", "dk", "dv")):
         check_grad(g, r, f"{n} {label}", mg, e)

@@ -393,7 +393,10 @@ def test_bwd_ex_validation(lib):
         assert bwd_ex(O(flags, -87.0, 0.0, 0, 0), causal=0, d=128) == -3, flags
     assert bwd_ex(O(alibi.CLAMP, float("nan"), 0.0, 0, 0)) == -1          # clamp not finite
     assert bwd_ex(O(64, 0.0, 0.0, 0, 0)) == -1                            # unknown bit
-    assert bwd_ex(O(alibi.SOFTCAP, 0.0, 50.0, 0, 0)) == -2                # forward-only forms
+    assert bwd_ex(O(alibi.SOFTCAP, 0.0, 50.0, 0, 0)) == -3                # soft cap accepted
+    assert bwd_ex(O(alibi.SOFTCAP | alibi.CLAMP, -87.0, 50.0, 0, 0), causal=0, d=128) == -3
+    for z in (0.0, -1.0, float("nan"), float("inf")):
+        assert bwd_ex(O(alibi.SOFTCAP, 0.0, z, 0, 0)) == -1, z            # cap not finite and positive
     assert bwd_ex(O(alibi.WINDOW, 0.0, 0.0, 0, 0, None, FAKE)) == -2
     assert bwd_ex(O(0, 0.0, 0.0, 5, 0)) == -2
     assert bwd_ex(O(alibi.CLAMP, -87.0, 0.0, 0, 0), d=96) == -2

@@ -198,6 +198,56 @@ def test_backward_mitigations(alibi, bwd_form, mit, B, H, N, d, causal):
     assert lerr <= LSE_TOL
 
 
+# (z, clamp, log distance): small caps keep tanh far from linear, so the
+# 1 - tanh^2 factor of the chain rule is tested, not approximated away
+CAPS = [(2.0, None, False), (3.0, -3.0, True), (50.0, None, False)]
+
+
+@pytest.mark.parametrize("cap", CAPS, ids=lambda c: f"z{c[0]:g}c{int(c[1] is not None)}l{int(c[2])}")
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 2, 300, 128, True), (1, 3, 129, 64, True), (2, 2, 200, 64, False), (1, 2, 513, 128, False),
+])
+def test_backward_softcap(alibi, bwd_form, cap, B, H, N, d, causal):
+    z, clamp, logd = cap
+    q, k, v, do = _inputs((B, H, N, d), 63)
+    s = oracle.slopes_recipe_ref("steep", H, logd)
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    out = alibi.attn_fwd_ex(qd, kd, vd, torch.from_numpy(s), causal, clamp=clamp, log_distance=logd, softcap=z,
+                            lse=lse)
+    dq, dk, dv = alibi.attn_bwd(qd, kd, vd, out, dod, lse, torch.from_numpy(s), causal, clamp=clamp,
+                                log_distance=logd, softcap=z)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    tag = f"softcap z={z:g} clamp={clamp} log={logd} B{B} H{H} N{N} d{d} causal={causal} qb={bwd_form}"
+    for b in range(B):
+        for h in range(H):
+            check_grads((dq[b, h], dk[b, h], dv[b, h]), q[b, h], k[b, h], v[b, h], do[b, h], float(s[h]), causal,
+                        f"{tag} b={b} h={h}", clamp=clamp, log_distance=logd, softcap=z)
+    lerr = np.abs(lse.cpu().double().numpy() - oracle.lse_ref(q, k, s, causal, clamp, logd, softcap=z)).max()
+    print(f"[parity] lse {tag}: max err {lerr:.2e}", flush=True)
+    assert lerr <= LSE_TOL
+
+
+def test_backward_softcap_paper_settings_full_size(alibi):
+    # the N = 4096, d = 128 sequence shape with the paper's cap (z = 50), floor
+    # (-87) and log-scaled distances (Sec. 4.3), 4 heads of one batch, every element
+    wl = W.FWD_B8_H16_N4096_D128
+    H = 4
+    q, k, v, do = _inputs((1, H, wl.N, wl.d), wl.seed + 5)
+    s = oracle.slopes_recipe_ref("explicit", H, True)
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    lse = torch.empty((1, H, wl.N), dtype=torch.float32, device="cuda")
+    out = alibi.attn_fwd_ex(qd, kd, vd, torch.from_numpy(s), True, clamp=-87.0, log_distance=True, softcap=50.0,
+                            lse=lse)
+    dq, dk, dv = alibi.attn_bwd(qd, kd, vd, out, dod, lse, torch.from_numpy(s), True, clamp=-87.0,
+                                log_distance=True, softcap=50.0)
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for h in range(H):
+        check_grads((dq[0, h], dk[0, h], dv[0, h]), q[0, h], k[0, h], v[0, h], do[0, h], float(s[h]), True,
+                    f"N4096 cap+clamp+log h={h}", clamp=-87.0, log_distance=True, softcap=50.0)
+
+
 def test_backward_mitigations_paper_settings_full_size(alibi):
     # the N = 4096, d = 128 sequence shape with the paper's floor (-87) and
     # log-scaled distances (Sec. 4.3), 8 heads of one batch, every element
