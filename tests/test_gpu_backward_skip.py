@@ -133,6 +133,8 @@ def test_backward_skip_flag_is_inert_elsewhere(alibi):
     _same(a, b, "clamp")
     a, b = _both(alibi, q, k, v, do, s, log_distance=True)
     _same(a, b, "log distance")
+    a, b = _both(alibi, q, k, v, do, s, softcap=5.0)
+    _same(a, b, "soft cap")
     out, lse = alibi.attn_fwd_train(q, k, v, s, False)
     a = alibi.attn_bwd(q, k, v, out, do, lse, s, False)
     b = alibi.attn_bwd(q, k, v, out, do, lse, s, False, skip_underflow=True)
