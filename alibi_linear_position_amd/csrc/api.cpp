@@ -185,10 +185,10 @@ int alibi_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, in
   if (d > 256 || d % 8 != 0) return ALIBI_ENOTSUP;
   const alibi::FwdArgs a{q, k, v, out, B, H, Nq, Nk, d, slopes, causal};
   if (d == 64 || d == 128) {
-    // Exact underflow skipping applies to the plain causal form; elsewhere the
-    // flag changes nothing (skipping is exact, so ignoring it is too).
+    // Exact underflow skipping applies to the plain form, causal or not;
+    // elsewhere the flag changes nothing (skipping is exact, so ignoring it is too).
     const bool mitigated = (opt.flags & (ALIBI_CLAMP | ALIBI_LOG_DISTANCE | ALIBI_SOFTCAP)) != 0;
-    if ((opt.flags & ALIBI_SKIP_UNDERFLOW) && causal && !mitigated) {
+    if ((opt.flags & ALIBI_SKIP_UNDERFLOW) && !mitigated) {
       const int parts = std::max(1, std::min(std::max(1, Nk / 256), (2048 + B * H - 1) / (B * H)));
       float* ws = nullptr;
       {

@@ -441,6 +441,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   constexpr int kTabPitch = 132;
   __shared__ __attribute__((aligned(16))) float ltab[(VAR & kVarLog) != 0 ? NW * 4 * kTabPitch : 4];
   int t_dead_wave = -1, t_dead = -1;
+  // Without the causal mask (symmetric bias): the first tile past the queries
+  // from which every key is dead too (2^30: none).
+  int t_rdead_wave = 1 << 30, t_rdead = 1 << 30;
+  __shared__ int s_rdead[NWG];
   // Hard window: keys j <= pi - W are out of row i's window. Tiles up to
   // t_wmask hold such a key for some row of the block and take the masked
   // path; tiles wholly out of a wave's window are dead for it, like the
@@ -448,8 +452,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
   const bool win_on = EXT && CAUSAL && VAR == 0 && var.window != nullptr;
   const int wwin = win_on ? max(-(1 << 30), min(var.window[h], 1 << 30)) : (1 << 30);
   int t_wmask = -1;
-  if (EXT && CAUSAL && VAR == 0 && ((var.knorm != nullptr && c2 > 0.0f) || win_on)) {
-    int td = -1;
+  if (EXT && VAR == 0 && ((var.knorm != nullptr && c2 > 0.0f) || win_on)) {
+    int td = -1, trd = 1 << 30;
     if (var.knorm != nullptr && c2 > 0.0f) {
     float kmax = 0.0f;
     for (int p = 0; p < var.parts; ++p) kmax = fmaxf(kmax, var.knorm[(long long)bh * var.parts + p]);
@@ -466,9 +470,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     // norms and their product carry a relative margin of 2^-8 against rounding
     const float A = sqrtf(sum_xor32(qn2)) * kmax * c1 * (1.0f + 1.0f / 256.0f);
     const float reach_f = (kDeadLog2 + 2.0f * A) / c2 + 1.0f;
-    const int reach = reach_f < 1.0e9f ? int(reach_f) + max(0, pi - Nk + 1) : (1 << 30);
+    // the row's nearest key lies at distance max(0, pi - Nk + 1) (and, without
+    // the mask, -pi for a row before every key); its score bounds the maximum
+    const int dnear = CAUSAL ? max(0, pi - Nk + 1) : max(max(0, pi - Nk + 1), -pi);
+    const int reach = reach_f < 1.0e9f ? int(reach_f) + dnear : (1 << 30);
     const int x = pi - reach;                                   // dead: j_max < x
     td = x >= 0 ? x / BN - 1 : -1;                               // last tile with j_max < x
+    if (!CAUSAL && reach < (1 << 30)) trd = (pi + reach) / BN + 1;  // first tile with j0 > pi + reach
     }
     if (win_on) {
       const int xw = pi - wwin + 1;                              // out of the window: j < xw
@@ -476,16 +484,28 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
       const int xb = min(q0 + BM, Nq) - 1 + delta - wwin + 1;    // the same for the block's last row
       t_wmask = xb >= 1 ? (xb - 1) / BN : -1;                    // tiles with j0 < xb
     }
-    if (i >= Nq) td = 1 << 30;                                   // rows past Nq do not count
+    if (i >= Nq) td = 1 << 30, trd = -1;                         // rows past Nq do not count
     td = min(td, __shfl_xor(td, 32, 64));
+    trd = max(trd, __shfl_xor(trd, 32, 64));
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) td = min(td, __shfl_xor(td, off, 64));
+    for (int off = 16; off >= 1; off >>= 1) {
+      td = min(td, __shfl_xor(td, off, 64));
+      trd = max(trd, __shfl_xor(trd, off, 64));
+    }
     t_dead_wave = max(__builtin_amdgcn_readfirstlane(td), -1);
-    if (lane == 0 && grp == 0) s_dead[wave] = t_dead_wave;  // wave w + 4 has the same rows
+    t_rdead_wave = __builtin_amdgcn_readfirstlane(trd);
+    if (lane == 0 && grp == 0) {
+      s_dead[wave] = t_dead_wave;  // wave w + 4 has the same rows
+      s_rdead[wave] = t_rdead_wave;
+    }
     __syncthreads();
     t_dead = s_dead[0];
+    t_rdead = s_rdead[0];
 #pragma unroll
-    for (int w2 = 1; w2 < NWG; ++w2) t_dead = min(t_dead, s_dead[w2]);
+    for (int w2 = 1; w2 < NWG; ++w2) {
+      t_dead = min(t_dead, s_dead[w2]);
+      t_rdead = max(t_rdead, s_rdead[w2]);
+    }
   }
 
   // Exponent of one score (log2 units) for the variants, from the plain
@@ -548,7 +568,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const unsigned char* sV = sK + KBYTES;
     unsigned char* const sKn = smem + (stage ^ 1) * STAGE;
     stage ^= 1;
-    if ((MASKED && !(qw0 < Nq && (!CAUSAL || j0 <= qw_last + delta))) || ((EXT || !MASKED) && tile <= t_dead_wave)) {
+    if ((MASKED && !(qw0 < Nq && (!CAUSAL || j0 <= qw_last + delta))) || ((EXT || !MASKED) && tile <= t_dead_wave) ||
+        (EXT && !CAUSAL && tile >= t_rdead_wave)) {
       regs.template store<KPITCH, VPITCH>(sKn, sKn + KBYTES, tid);
       return;
     }
@@ -885,11 +906,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(
     const int ql = q0 + BM - 1 + delta;                          // last query position of the block
     const int tr = max(tl + 1, ql <= 0 ? 0 : (ql + BN - 1) / BN);  // right tiles tr .. nfull - 1
     const int mid_hi = min(tr, nfull) - 1;                        // middle tiles tl + 1 .. mid_hi
-    const int after_mid = tr < nfull ? tr : tl;
+    // exact skipping: the right tiles end before t_rdead, the left ones after t_dead
+    const int r_end = min(nfull, max(t_rdead, tr));
+    const int after_mid = tr < r_end ? tr : tl;
     if (Nk % BN != 0) step(nfull, mid_hi > tl ? mid_hi : after_mid, Masked{});
     for (int t = mid_hi; t > tl; --t) step(t, t - 1 > tl ? t - 1 : after_mid, Masked{});
-    for (int t = tr; t < nfull; ++t) step(t, t + 1 < nfull ? t + 1 : tl, Right{});
-    for (int t = tl; t >= 0; --t) step(t, t - 1, Left{});
+    for (int t = tr; t < r_end; ++t) step(t, t + 1 < r_end ? t + 1 : tl, Right{});
+    for (int t = tl; t > t_dead; --t) step(t, t - 1, Left{});
   }
 
   if constexpr (SPLIT == 2) {

@@ -349,6 +349,11 @@ def next_forms(alibi, q, k, v, s, fw):
     ms = time_launches(lambda: alibi.attn_fwd(q, k, v, s, causal=False, out=out))
     res["non_causal"] = {"value": round(4.0 * d * B * H * N * N / ms / 1e9, 1), "unit": "TFLOP/s",
                          "ms": round(ms, 4)}
+    ms = time_launches(lambda: alibi.attn_fwd_ex(q, k, v, s, False, skip_underflow=True, out=out))
+    res["non_causal_skip_underflow"] = {"value": round(4.0 * d * B * H * N * N / ms / 1e9, 1),
+                                        "unit": "TFLOP/s (unskipped flops)", "ms": round(ms, 4),
+                                        "note": "the symmetric bias -m|i-j| with exact skipping on both sides of "
+                                                "each query block; key-norm pass included"}
     ms = time_launches(lambda: alibi.attn_fwd_ex(q, k, v, s, True, skip_underflow=True, out=out))
     res["skip_underflow"] = {"value": round(causal_flops / ms / 1e9, 1), "unit": "TFLOP/s (causal flops)",
                              "ms": round(ms, 4),

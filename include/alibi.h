@@ -221,10 +221,11 @@ int alibi_attn_weights_f32(const float* q, const float* k, float* w,
  * (b, h) in a library-owned per-device workspace; the forward then bounds each
  * score by |q_i| max|k| / sqrt(d) - m (i - j) and stops, per workgroup, at the
  * first key tile where that bound lies more than 148 log2 units under the
- * row's guaranteed running maximum. The output is bit-identical to the call
- * without the flag. It acts on the plain causal form with d in {64, 128}; with
- * mitigations, without the causal mask or on the generic kernel it is accepted
- * and changes nothing. Calls with this flag on one device share the workspace:
+ * row's guaranteed running maximum (without the causal mask, the symmetric
+ * bias -m |i - j| lets it stop on both sides of the queries). The output is
+ * bit-identical to the call without the flag. It acts on the plain form with
+ * d in {64, 128}, causal or not; with mitigations or on the generic kernel it
+ * is accepted and changes nothing. Calls with this flag on one device share the workspace:
  * order them on one stream (or synchronise between them).
  */
 #define ALIBI_SKIP_UNDERFLOW 8
