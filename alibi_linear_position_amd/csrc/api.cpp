@@ -247,10 +247,11 @@ int alibi_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o
     skip = (opts->flags & ALIBI_SKIP_UNDERFLOW) != 0;
   }
   if (d != 64 && d != 128) return ALIBI_ENOTSUP;
-  // Exact underflow skipping acts on the plain causal form (elsewhere the flag
-  // changes nothing); its bound needs the largest query and key norms per
-  // (b, h), kept as partial maxima behind the row terms in the workspace.
-  skip = skip && causal && flags == 0;
+  // Exact underflow skipping acts on the plain form, causal or not (with the
+  // mitigations the flag changes nothing); its bound needs the largest query
+  // and key norms per (b, h), kept as partial maxima behind the row terms in
+  // the workspace.
+  skip = skip && flags == 0;
   const long long bh = (long long)B * H;
   const int parts = skip ? int(std::max(1LL, std::min(std::max(1LL, (long long)N / 256), (2048 + bh - 1) / bh))) : 0;
   float* ws = nullptr;

@@ -267,11 +267,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // per-lane byte offsets of the swizzled tile reads
   const int rb = Tile::row_base(lane), tb0 = Tile::tr_base(lane, 0), tb1 = Tile::tr_base(lane, 1);
 
-  const int qt0 = CAUSAL ? k0 / BQ : 0;
-  // Underflow skipping: queries more than R past a key give it P = 0 exactly,
+  // Underflow skipping: queries more than R from a key give it P = 0 exactly,
   // so the tiles whose first query lies past the block's last key + R (and
-  // all after them) are dropped, and a wave skips the tiles past its own keys'.
-  const int R = CAUSAL && VAR == 0 ? live_reach(norms, parts, total / nkb, bh, c1, c2) : (1 << 30);
+  // all after them) are dropped, without the causal mask also those whose
+  // last query lies more than R before its first key (and all before them),
+  // and a wave skips the tiles that far from its own keys.
+  const int R = VAR == 0 ? live_reach(norms, parts, total / nkb, bh, c1, c2) : (1 << 30);
+  int qt0 = CAUSAL ? k0 / BQ : 0;
+  if (!CAUSAL && R < (1 << 30) && k0 - R > 0) qt0 = (k0 - R) / BQ;  // tile of the first live query
   int nqt = (N + BQ - 1) / BQ;
   if (R < (1 << 30)) nqt = min(nqt, (k0 + BK - 1 + R) / BQ + 1);
 
@@ -464,7 +467,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       if (t == nqt) return;
       const unsigned char* st = stage_of(t);
       const int q0 = t * BQ;
-      if (!CAUSAL || ((OPEN || q0 + BQ - 1 >= kw0) && q0 - (kw0 + 31) <= R)) {
+      if (CAUSAL ? ((OPEN || q0 + BQ - 1 >= kw0) && q0 - (kw0 + 31) <= R)
+                 : (kw0 - (q0 + BQ - 1) <= R && q0 - (kw0 + 31) <= R)) {
         f32x16 p[QB], gcap[QB];
         products(st, kf, cinit, p);
         const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
@@ -504,7 +508,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const unsigned char* st = stage_of(u);
       const float* sL = reinterpret_cast<const float*>(st + 2 * RBYTES);
       const int q0 = u * BQ;
-      if (!CAUSAL || (q0 + BQ - 1 >= kw0 && q0 - (kw0 + 31) <= R)) {  // the dV wave's test
+      if (CAUSAL ? (q0 + BQ - 1 >= kw0 && q0 - (kw0 + 31) <= R)  // the dV wave's test
+                 : (kw0 - (q0 + BQ - 1) <= R && q0 - (kw0 + 31) <= R)) {
         f32x16 dp[QB];
         products(st + RBYTES, vf, f32x16{}, dp);
 #pragma unroll
@@ -602,11 +607,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int ntiles = (kend + BN - 1) / BN;
   // Underflow skipping: key tiles whose last key lies more than R before the
   // block's first query carry P = 0 exactly for every query of the block: the
-  // walk stops above them (t_lo), and a wave skips the tiles that far before
-  // its own first query.
-  const int R = CAUSAL && VAR == 0 ? live_reach(norms, parts, total / nqb, bh, c1, c2) : (1 << 30);
+  // walk stops above them (t_lo); without the causal mask it also starts below
+  // the tiles whose first key lies more than R after the block's last query
+  // (t_hi); and a wave skips the tiles that far from its own queries.
+  const int R = VAR == 0 ? live_reach(norms, parts, total / nqb, bh, c1, c2) : (1 << 30);
   const int xdead = q0 - BN - R;  // tiles with j0 <= xdead are dead
   const int t_lo = R < (1 << 30) && xdead >= 0 ? xdead / BN + 1 : 0;
+  const int t_hi = !CAUSAL && R < (1 << 30) ? min(ntiles - 1, (q0 + BM - 1 + R) / BN) : ntiles - 1;
 
   u32x4 rk[LOADS], rv[LOADS];
   // chunk tid + NT r of a tile: byte 16 (tid + NT r) past its first row; rows
@@ -632,7 +639,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   };
 
   if (ntiles > 0) {
-    load_tile((ntiles - 1) * BN);
+    load_tile(t_hi * BN);
     store_tile(smem);
   }
   // Tiles wholly at or before the block's first query (and below N) need no
@@ -649,7 +656,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const unsigned char* st = smem + stage * STAGE;
     const unsigned char* sK = st;
     const unsigned char* sV = st + KBYTES;
-    const bool active = qw0 < N && (!CAUSAL || ((OPEN || j0 <= qw_last) && qw0 - (j0 + BN - 1) <= R));
+    const bool active = qw0 < N && (CAUSAL ? ((OPEN || j0 <= qw_last) && qw0 - (j0 + BN - 1) <= R)
+                                           : (qw0 - (j0 + BN - 1) <= R && j0 - (qw0 + 31) <= R));
     if (active) {
       // ---- per 32-key block: S^T = K Q^T, dP^T = V dO^T (lane = query), then
       // P^T = exp2(t - lse2) and dS^T = P^T (dP^T - D) packed to bf16 ----
@@ -713,7 +721,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   };
   const int x_open = q0 + 1;  // keys [0, x_open) are at or before every query of the block
   const int t_open = x_open < BN ? -1 : min(min(x_open / BN - 1, N / BN - 1), ntiles - 1);
-  int tile = ntiles - 1;
+  int tile = t_hi;
   for (; tile > max(t_open, t_lo - 1); --tile) step(tile, std::false_type{});
   for (; tile >= t_lo; --tile) step(tile, std::true_type{});
 

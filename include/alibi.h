@@ -316,8 +316,8 @@ int alibi_attn_bwd(const void* q, const void* k, const void* v, const void* out,
  * ALIBI_WINDOW and nonzero offsets: ALIBI_ENOTSUP (forward-only forms);
  * unknown bits, a non-finite clamp or a soft cap that is not finite and
  * positive: ALIBI_EINVAL.
- * ALIBI_SKIP_UNDERFLOW (plain causal form; accepted and without effect with
- * the mitigations or without the causal mask): a first pass takes max|q_i|
+ * ALIBI_SKIP_UNDERFLOW (plain form, causal or not; accepted and without
+ * effect with the mitigations): a first pass takes max|q_i|
  * and max|k_j| per (b, h); every logit is then at most A - m D (A =
  * max|q| max|k| / sqrt(d)) and every row's log-sum-exp at least -A (its
  * diagonal logit), so query-key pairs further apart than D with

@@ -142,3 +142,40 @@ def test_backward_skip_flag_is_inert_elsewhere(alibi):
     z = torch.zeros(4, dtype=torch.float32)                  # zero slopes: nothing to skip
     a, b = _both(alibi, q, k, v, do, z)
     _same(a, b, "zero slopes")
+
+
+@pytest.mark.parametrize("B,H,N,d,recipe", [
+    (1, 8, 2048, 128, "steep"),
+    (2, 3, 1000, 64, "steep"),
+    (1, 16, 4096, 128, None),
+])
+def test_backward_skip_non_causal_is_bit_exact(alibi, bwd_form, B, H, N, d, recipe):
+    # the symmetric bias -m |i - j|: tiles far on either side carry zero P
+    q, k, v, do = (dev(x) for x in _inputs((B, H, N, d), 46))
+    s = alibi.slopes(H) if recipe is None else alibi.slopes_recipe(recipe, H)
+    out, lse = alibi.attn_fwd_train(q, k, v, s, False)
+    a = alibi.attn_bwd(q, k, v, out, do, lse, s, False)
+    b = alibi.attn_bwd(q, k, v, out, do, lse, s, False, skip_underflow=True)
+    torch.cuda.synchronize()
+    _same(a, b, f"non-causal B{B} H{H} N{N} d{d} {recipe} qb={bwd_form}")
+
+
+def test_backward_skip_non_causal_really_skips(alibi):
+    # NaN in dO of the middle row: the full backward spreads it to every key,
+    # the skipping one only to keys near that row, on both sides
+    B, H, N, d = 1, 2, 2048, 128
+    q, k, v, do = _inputs((B, H, N, d), 47)
+    i = N // 2
+    do[:, :, i, 0] = float("nan")
+    q, k, v, do = dev(q), dev(k), dev(v), dev(do)
+    s = alibi.slopes_recipe("steep", H)
+    out, lse = alibi.attn_fwd_train(q, k, v, s, False)
+    _, dk_full, _ = alibi.attn_bwd(q, k, v, out, do, lse, s, False)
+    dq, dk, dv = alibi.attn_bwd(q, k, v, out, do, lse, s, False, skip_underflow=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(dk_full.float()).any(-1).all()
+    nan_keys = torch.isnan(dk.float()).any(-1)[0]           # (H, N)
+    assert nan_keys[:, i].all()
+    print(f"[skip] non-causal keys left finite: {int((~nan_keys).sum())} of {H * N}", flush=True)
+    assert not nan_keys[:, :64].any() and not nan_keys[:, -64:].any()   # both ends are never visited
+    assert torch.equal(torch.isnan(dv.float()).any(-1)[0], nan_keys)
