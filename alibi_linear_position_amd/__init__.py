@@ -266,7 +266,7 @@ def attn_bwd(q, k, v, out, dout, lse, slopes=None, causal=True, clamp=None, log_
     """Gradients (dq, dk, dv), bf16 (B, H, N, d), of the plain forward, or of the
     forward with the clamp, the log-distance bias and/or the soft cap z (lse from
     attn_fwd_ex with the same settings). skip_underflow: exact skipping of the
-    query-key tiles whose every P rounds to zero (plain causal form;
+    query-key tiles whose every P rounds to zero (plain form;
     bit-identical gradients)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):

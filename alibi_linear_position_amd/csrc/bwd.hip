@@ -38,8 +38,8 @@
 // P (1 - tanh^2) to the dK waves, and the dQ kernel scales its dS). The
 // scores are then not seeded and the logit is formed per score.
 //
-// With the per-(b, h) norm maxima of Q and K (plain causal form), both
-// kernels end their walks, and each wave skips its own tiles, at the distance
+// With the per-(b, h) norm maxima of Q and K (plain form, causal or not),
+// both kernels end their walks, and each wave skips its own tiles, at the distance
 // past which every P is an exact zero (live_reach below): the gradients keep
 // every bit.
 #include "device_common.h"
@@ -156,7 +156,7 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int base) {
   return r;
 }
 
-// Exact underflow skipping of the plain causal form. With M_q and M_k the
+// Exact underflow skipping of the plain form. With M_q and M_k the
 // largest query and key norms of a (b, h) pair and A = c1 M_q M_k, every
 // logit (log2 units) is at most A - c2 D at distance D = i - j
 // (Cauchy-Schwarz on the content term) and every row's log-sum-exp is at

@@ -266,7 +266,7 @@ struct FwdVariant {
   float cap_out;  // z log2(e)
   float cap_small;  // largest |s| with |A| <= z / 4
   float cap_q[3];   // z log2(e) tanh(A / z) ~ s (q0 + q1 s^2 + q2 s^4) for |A| <= z / 4
-  // Exact underflow skipping (plain causal form only): `parts` partial maxima
+  // Exact underflow skipping (plain form): `parts` partial maxima
   // of the key norms of each (b, h), or null.
   const float* knorm;
   int parts;

@@ -61,7 +61,7 @@ struct BwdArgs {
   // s = q.k, and the capped logit z tanh(A / z) in log2 units is cap_out tanh(A / z)
   float cap_in = 0.0f;
   float cap_out = 0.0f;
-  // exact underflow skipping (plain causal form): P partial maxima of the key
+  // exact underflow skipping (plain form): P partial maxima of the key
   // norms of every (b, h), then those of the query norms (launch_knorm_max),
   // or null for no skipping
   const float* norms = nullptr;
